@@ -1,0 +1,27 @@
+"""CPU oracle for blockwise ring attention — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke entry point and the benchmark's CPU-baseline leg may import this
+package.  The product path (the HIP library and its Python binding) never imports, calls or links
+anything here, and this package imports nothing from the product path: the two share no code.
+
+What is here, in float64 NumPy:
+
+* :func:`attention_reference` — the plain definition of (causal or full) softmax attention with
+  log-sum-exp, written out directly.  The pages state that the ring method reaches exactly this
+  result, so it is the oracle for every GPU parity test.
+* :func:`attention_rows` — the same definition evaluated only on chosen (batch, head, token) rows,
+  for workloads too large for the full O(S^2) computation.
+* :func:`ring_replay` — the ring schedule with the online-softmax fold, in the pages' order and
+  notation, used to check the method's own claims (exactness, arrival-order invariance) on the CPU.
+* :mod:`oracle.layout` — contiguous and striped token-to-shard assignment.
+
+Every function is pinned by CPU tests to facts outside itself (the pages' demonstration, library
+routines, closed forms, brute force); none is "parity unpinned".
+"""
+from .attention import attention_reference, attention_rows, ring_replay
+from .layout import shard_positions, striped_permutation, contiguous_permutation
+
+__all__ = [
+    "attention_reference", "attention_rows", "ring_replay",
+    "shard_positions", "striped_permutation", "contiguous_permutation",
+]
