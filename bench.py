@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-device ring-attention hot path on one MI355X.
+
+One benchmark step = one call of ``ring_attn_local``: the whole P-step ring (hop copies on a
+second stream, one batched step kernel per ring step, the final division fused into each device's
+last step) over one batch of seeded synthetic input already resident in HBM.
+
+The default workload is the non-causal bf16 configuration the headline metric is quoted on
+(B=1, S=16384 as 8 shards of 2048, 8 heads, D=128, all 8 devices on the one GPU).  The causal
+striped grouped-query configuration (S=65536, 32 query / 8 key-value heads) is reported under
+"extra" in the same JSON line.
+
+FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
+runs count only the visible pairs.  Printed on stdout: one JSON line.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s on 1 MI355X (causal & non-causal) + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_SOURCE = os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", "step_mfma_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def shard_np(x, P, layout):
+    """[B, S, H, D] token order -> [P, B, n, H, D] shard order (host-side layout step)."""
+    import numpy as np
+    B, S, H, D = x.shape
+    n = S // P
+    if layout == "striped":
+        y = x.reshape(B, n, P, H, D).transpose(2, 0, 1, 3, 4)  # token r*P + i -> shard i, row r
+    else:
+        y = x.reshape(B, P, n, H, D).transpose(1, 0, 2, 3, 4)
+    return np.ascontiguousarray(y)
+
+
+def run_workload(w, steps, warmup):
+    import numpy as np
+    import torch
+
+    import blockwise_ring_attention_step_amd as ra
+    import synth_inputs as si
+
+    t0 = time.time()
+    q, k, v = si.workload_qkv(w)
+    n = w.n
+    if w.local_shard is None:
+        qs = shard_np(q, w.P, w.layout)
+        dev0, n_local = 0, w.P
+    else:
+        qs = np.ascontiguousarray(q.reshape(w.B, 1, n, w.Hq, w.D).transpose(1, 0, 2, 3, 4))
+        dev0, n_local = w.local_shard, 1
+    ks, vs = shard_np(k, w.P, w.layout), shard_np(v, w.P, w.layout)
+    del q, k, v
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    tq, tk, tv = up(qs), up(ks), up(vs)
+    del qs, ks, vs
+    o = torch.empty_like(tq)
+    lse = torch.empty((n_local, w.B, w.Hq, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(w.P, n_local, w.B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs generated and uploaded in {time.time() - t0:.1f}s")
+
+    cs = torch.cuda.Stream()
+    xs = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(w.D)
+    causal = w.causal
+    striped = w.layout == "striped"
+
+    def call(events=None):
+        ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=causal, striped=striped,
+                           compute_stream=cs, copy_stream=xs, step_events=events)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[ra.HipEvent() for _ in range(2 * w.P)] for _ in range(steps)]
+    start, end = ra.HipEvent(), ra.HipEvent()
+    torch.cuda.synchronize()
+    start.record(cs)
+    for i in range(steps):
+        call(ev[i])
+    end.record(cs)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_ms(end)
+    ms = total_ms / steps
+
+    # algorithmic FLOPs per ring step launch (all local devices of that step)
+    per_launch = []
+    for s in range(w.P):
+        pairs = 0
+        for i in range(dev0, dev0 + n_local):
+            pairs += ra.ring_attn_visible_pairs(w.P, n, i, (i - s) % w.P, causal=causal, striped=striped)
+        per_launch.append(4.0 * w.D * w.Hq * w.B * pairs)
+    flops = sum(per_launch)
+    assert abs(flops - w.flops()) <= 1e-6 * flops, (flops, w.flops())
+    kernel_ms = [[ev[i][2 * s].elapsed_ms(ev[i][2 * s + 1]) for s in range(w.P)] for i in range(steps)]
+    launch_ms = [sum(kernel_ms[i][s] for i in range(steps)) / steps for s in range(w.P)]
+    kernel_total_ms = sum(launch_ms)
+    achieved = flops / (kernel_total_ms * 1e-3) / 1e12  # flop-weighted average over the step launches
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
+        f"step kernels {kernel_total_ms:.3f} ms ({achieved:.1f} TFLOP/s), per step "
+        + ", ".join(f"{x:.3f}" for x in launch_ms))
+    res = dict(workload=w.name, ms=ms, tflops=tflops, flops=flops, kernel_ms=kernel_total_ms,
+               kernel_tflops=achieved, launch_ms=launch_ms, launch_flops=per_launch)
+    del tq, tk, tv, o, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def traffic_entry():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it belongs to this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """Time the float64 CPU oracle on a bounded sample of the workload's query rows."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs as si
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    if w.local_shard is not None or w.layout != "contiguous":
+        raise ValueError("the CPU baseline samples token-order queries of a whole-sequence workload")
+    q, k, v = si.workload_qkv(w)
+    qf, kf, vf = si.bf16_to_f32(q), si.bf16_to_f32(k), si.bf16_to_f32(v)
+    rng = np.random.default_rng(7)
+
+    def sample(nrows):
+        t = rng.choice(q.shape[1], size=nrows, replace=False)
+        h = rng.integers(0, w.Hq, size=nrows)
+        return np.stack([np.zeros(nrows, dtype=np.int64), h, t], axis=1)
+
+    def visible(rows):
+        if not w.causal:
+            return float(len(rows) * w.S)
+        return float(np.sum(rows[:, 2] + 1))  # contiguous token order: query t sees t+1 keys
+
+    rows = sample(64)
+    t0 = time.time()
+    oracle.attention_rows(qf, kf, vf, rows, causal=w.causal)
+    dt = time.time() - t0
+    nrows = int(min(q.shape[1] * w.Hq, max(64, 64 * seconds / max(dt, 1e-3))))
+    rows = sample(nrows)
+    t0 = time.time()
+    oracle.attention_rows(qf, kf, vf, rows, causal=w.causal)
+    dt = time.time() - t0
+    fl = 4.0 * w.D * visible(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{nrows} random (head, token) rows of {w.name}, float64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="noncausal_16k")
+    ap.add_argument("--extra", default="causal_striped_64k",
+                    help="comma-separated extra workloads reported under 'extra' ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the ring; runs on more than one GPU are not supported "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = si.WORKLOADS[args.workload]
+    main_res = run_workload(w, args.steps, args.warmup)
+    extras = []
+    for name in [x for x in args.extra.split(",") if x]:
+        r = run_workload(si.WORKLOADS[name], max(3, args.steps // 2), args.warmup)
+        extras.append({"workload": name, "value": r["tflops"], "unit": "TFLOP/s", "ms_per_step": r["ms"],
+                       "pct_of_peak": 100 * r["tflops"] / PEAK_BF16_TFLOPS, "step_kernel_tflops": r["kernel_tflops"],
+                       "causal": si.WORKLOADS[name].causal, "layout": si.WORKLOADS[name].layout})
+
+    traffic = traffic_entry()
+    roof = {"bound": "mfma", "kernel": "step_mfma_bf16_d128", "achieved": main_res["kernel_tflops"],
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": main_res["kernel_tflops"] / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch": main_res["launch_flops"][0], "avg_launch_ms": sum(main_res["launch_ms"]) / w.P}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": main_res["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "P": w.P, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "mask": "causal" if w.causal else "none", "layout": w.layout,
+                   "hops": "device-to-device copies on a second stream, double-buffered"},
+        "pct_of_peak": 100 * main_res["tflops"] / PEAK_BF16_TFLOPS,
+        "roofline": roof, "cpu_baseline": cpu, "extra": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

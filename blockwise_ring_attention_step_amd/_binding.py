@@ -1,0 +1,203 @@
+"""ctypes binding of libringattn.so: argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILE = os.path.join(_PKG_DIR, "libringattn.so")
+
+RA_F32, RA_BF16 = 0, 1
+RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
+RA_STEP_INIT = 1
+RA_MAX_DEV, RA_MAX_D = 64, 128
+
+EXPORTED_SYMBOLS = (
+    "ring_attn_step", "ring_attn_finalize", "ring_attn_local", "ring_attn_local_workspace_bytes",
+    "ring_attn_plan", "ring_attn_visible_pairs", "ring_attn_strerror",
+)
+
+_lib = None
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {code} ({ring_attn_strerror(code)})")
+        self.code = code
+
+
+def lib_path() -> str:
+    return _LIB_FILE
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (built by ``blockwise_ring_attention_step_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_FILE):
+        raise RuntimeError(f"{_LIB_FILE} is missing: build it with `python -m blockwise_ring_attention_step_amd.build`")
+    L = ctypes.CDLL(_LIB_FILE)
+    i32, i64, f32, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    L.ring_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, p64, i64,
+                                 p64, i64, i32, vp]
+    L.ring_attn_step.restype = i32
+    L.ring_attn_finalize.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.ring_attn_finalize.restype = i32
+    L.ring_attn_local.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                  vp, sz, vp, vp, vp]
+    L.ring_attn_local.restype = i32
+    L.ring_attn_local_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.ring_attn_local_workspace_bytes.restype = sz
+    L.ring_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+    L.ring_attn_plan.restype = i32
+    L.ring_attn_visible_pairs.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.ring_attn_visible_pairs.restype = i64
+    L.ring_attn_strerror.argtypes = [i32]
+    L.ring_attn_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def ring_attn_strerror(code: int) -> str:
+    return lib().ring_attn_strerror(int(code)).decode()
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise RingAttnError(fn, rc)
+
+
+def _ptr(t):
+    """Device pointer of a CUDA tensor (or None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i64_array(xs):
+    if xs is None:
+        return None
+    arr = (ctypes.c_int64 * len(xs))(*[int(x) for x in xs])
+    return arr
+
+
+def ring_attn_step(q, k, v, o_acc, m, l, *, scale, causal=False, q_off=None, q_stride=1, k_off=None, k_stride=1,
+                   init=False, stream=None):
+    """Fold the key/value blocks k, v into the state (o_acc, m, l) of the query blocks q.
+
+    q [n_dev, B, Nq, Hq, D], k/v [n_dev, B, Nk, Hkv, D] (bf16 or fp32); o_acc [n_dev, B, Hq, Nq, D],
+    m/l [n_dev, B, Hq, Nq] fp32.  q_off/k_off: per-device position offsets (sequences of ints).
+    """
+    n_dev, B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[2], k.shape[3]
+    rc = lib().ring_attn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(m), _ptr(l), n_dev, B, Hq, Hkv, Nq, Nk, D,
+                              _dtype_code(q), float(scale), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+                              _i64_array(q_off), int(q_stride), _i64_array(k_off), int(k_stride),
+                              RA_STEP_INIT if init else 0, _stream(stream))
+    _check("ring_attn_step", rc)
+
+
+def ring_attn_finalize(o_acc, m, l, o, lse=None, *, stream=None):
+    """o = o_acc / l in token-major layout [n_dev, B, Nq, Hq, D]; lse = ln(sum exp(scores)) [n_dev, B, Hq, Nq]."""
+    n_dev, B, Hq, Nq, D = o_acc.shape
+    rc = lib().ring_attn_finalize(_ptr(o_acc), _ptr(m), _ptr(l), _ptr(o), _ptr(lse), n_dev, B, Hq, Nq, D,
+                                  _dtype_code(o), _stream(stream))
+    _check("ring_attn_finalize", rc)
+
+
+def ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype):
+    return int(lib().ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype))
+
+
+def ring_attn_local(q_local, k_src, v_src, o, lse, workspace, *, P, dev0, scale, causal=False, striped=False,
+                    compute_stream=None, copy_stream=None, step_events=None):
+    """Run the whole P-step ring for the local devices [dev0, dev0 + n_local).
+
+    q_local [n_local, B, n, Hq, D]; k_src/v_src [P, B, n, Hkv, D] (device tensors, or pinned host
+    tensors); o like q_local; lse [n_local, B, Hq, n] fp32 or None; workspace: uint8 device tensor.
+    step_events: optional list of 2*P HipEvent objects recorded around each step kernel.
+    """
+    n_local, B, n, Hq, D = q_local.shape
+    Hkv = k_src.shape[3]
+    host_src = not k_src.is_cuda
+    if host_src and not (k_src.is_pinned() and v_src.is_pinned()):
+        raise ValueError("host key/value sources must be pinned")
+    kp = k_src.data_ptr() if host_src else _ptr(k_src)
+    vp = v_src.data_ptr() if host_src else _ptr(v_src)
+    ev = None
+    if step_events is not None:
+        if len(step_events) != 2 * P:
+            raise ValueError("step_events needs 2*P events")
+        ev = (ctypes.c_void_p * (2 * P))(*[e.handle for e in step_events])
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    rc = lib().ring_attn_local(_ptr(q_local), kp, vp, 1 if host_src else 0, _ptr(o), _ptr(lse), P, dev0, n_local, B,
+                               Hq, Hkv, n, D, _dtype_code(q_local), float(scale),
+                               RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+                               RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), cs, xs, ev)
+    _check("ring_attn_local", rc)
+
+
+def ring_attn_plan(P, dev0, n_local, n, *, causal=False, striped=False) -> np.ndarray:
+    """Schedule table [P * n_local, 5] of (step, device, block, slot, class)."""
+    out = np.zeros((P * n_local, 5), dtype=np.int32)
+    rc = lib().ring_attn_plan(P, dev0, n_local, n, RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+                              RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS,
+                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    _check("ring_attn_plan", rc)
+    return out
+
+
+def ring_attn_visible_pairs(P, n, i, j, *, causal=False, striped=False) -> int:
+    r = lib().ring_attn_visible_pairs(P, n, RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+                                      RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS, i, j)
+    if r < 0:
+        raise RingAttnError("ring_attn_visible_pairs", -1)
+    return int(r)
+
+
+class HipEvent:
+    """A timing hipEvent_t (owned by a torch.cuda.Event) whose raw handle the library can record."""
+
+    def __init__(self):
+        import torch
+        self._ev = torch.cuda.Event(enable_timing=True)
+        self._ev.record(torch.cuda.current_stream())  # creates the underlying hipEvent_t
+        self.handle = self._ev.cuda_event
+        if not self.handle:
+            raise RuntimeError("could not create a HIP event")
+
+    def record(self, stream=None):
+        import torch
+        self._ev.record(torch.cuda.current_stream() if stream is None else stream)
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        return float(self._ev.elapsed_time(end._ev))

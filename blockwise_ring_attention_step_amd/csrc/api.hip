@@ -1,0 +1,452 @@
+// C ABI of the ring-attention library: argument validation, the ring schedule (planner), the step
+// and finalize entry points and the whole-ring driver with its copy/compute overlap.
+//
+// The schedule follows the Ultralytics glossary page "Ring Attention", section "Como funciona a
+// atenção em anel": P steps; in step s device i holds key/value block j = (i - s) mod P, which it
+// received from device i - 1 (the block that device held one step earlier).  The hop for step s+1
+// runs on a second stream while step s computes, as "Ring Attention Là Gì?" (thienlv.com), section
+// "Ring Attention Hoạt Động Thế Nào?", describes (the next block is already being sent during the
+// current computation).  Causal blocks that are fully masked are skipped, which is the idle time of
+// the first devices that the Ultralytics page attributes to causal masking.
+#include <cmath>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+using ra::StepParams;
+
+constexpr double kLog2e = 1.4426950408889634;
+
+size_t elem_size(int dtype) { return dtype == RA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dtype) { return dtype == RA_F32 || dtype == RA_BF16; }
+
+// [a, a + na) and [b, b + nb) overlap (empty ranges never overlap)
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+// product of non-negative sizes, or -1 on overflow past 2^62
+int64_t mul_sizes(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && r > ((int64_t)1 << 62) / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+// Position of the first and last row of a block: off + r * stride.
+struct Span {
+  int64_t lo, hi;
+};
+
+// Classification of a (query block, key block) pair from positions.
+// 0: no key visible to any query; 1: every key visible to every query; 2: partially visible.
+int classify(bool causal, int64_t q_off, int64_t q_stride, int Nq, int64_t k_off, int64_t k_stride, int Nk) {
+  if (Nq <= 0 || Nk <= 0) return 0;
+  if (!causal) return 1;
+  const Span q{q_off, q_off + (int64_t)(Nq - 1) * q_stride};
+  const Span k{k_off, k_off + (int64_t)(Nk - 1) * k_stride};
+  if (k.lo > q.hi) return 0;
+  if (k.hi <= q.lo) return 1;
+  return 2;
+}
+
+int64_t block_offset(int layout, int P, int n, int block) {
+  return layout == RA_LAYOUT_STRIPED ? (int64_t)block : (int64_t)block * n;
+}
+
+int64_t layout_stride(int layout, int P) { return layout == RA_LAYOUT_STRIPED ? (int64_t)P : 1; }
+
+int64_t count_visible(int P, int n, int mask, int layout, int i, int j) {
+  if (n <= 0) return 0;
+  if (mask == RA_MASK_NONE) return (int64_t)n * n;
+  const int64_t qo = block_offset(layout, P, n, i), ko = block_offset(layout, P, n, j);
+  const int64_t st = layout_stride(layout, P);
+  // number of key rows u in [0, n) with ko + u*st <= qo + r*st, summed over query rows r
+  int64_t total = 0;
+  for (int r = 0; r < n; ++r) {
+    const int64_t d = qo + (int64_t)r * st - ko;
+    if (d < 0) continue;
+    const int64_t c = d / st + 1;
+    total += c < n ? c : n;
+  }
+  return total;
+}
+
+struct Shape {
+  int n_dev, B, Hq, Hkv, Nq, Nk, D, dtype;
+};
+
+int validate_shape(const Shape& s) {
+  if (s.n_dev < 1 || s.n_dev > RA_MAX_DEV) return RA_ERR_INVALID_ARG;
+  if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.Nq < 0 || s.Nk < 0 || s.D < 1) return RA_ERR_INVALID_ARG;
+  if (s.Hq % s.Hkv) return RA_ERR_INVALID_ARG;
+  if (!valid_dtype(s.dtype)) return RA_ERR_INVALID_ARG;
+  if (s.D > RA_MAX_D) return RA_ERR_UNSUPPORTED;
+  if (mul_sizes({s.n_dev, s.B, s.Nq, s.Hq, s.D}) < 0 || mul_sizes({s.n_dev, s.B, s.Nk, s.Hkv, s.D}) < 0)
+    return RA_ERR_INVALID_ARG;
+  return RA_OK;
+}
+
+// Fill the work decomposition fields and launch the right kernel for the devices in p.
+hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream) {
+  if (p.n_launch == 0 || p.Nq == 0) return hipSuccess;
+  if (dtype == RA_BF16 && p.D == 128) {
+    p.groups = p.n_launch * p.B * p.Hkv;
+    p.groups_per_xcd = (p.groups + 7) / 8;
+    p.n_qtiles = (p.Nq + 127) / 128;
+    return ra::launch_step_mfma_bf16_d128(p, stream);
+  }
+  return ra::launch_step_generic(p, dtype, stream);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RA_OK : RA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ring_attn_strerror(int code) {
+  switch (code) {
+    case RA_OK: return "ok";
+    case RA_ERR_INVALID_ARG: return "invalid argument";
+    case RA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RA_ERR_HIP: return "HIP runtime error";
+    case RA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j) {
+  if (P < 1 || P > RA_MAX_DEV || n < 0 || i < 0 || j < 0 || i >= P || j >= P) return -1;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return -1;
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return -1;
+  return count_visible(P, n, mask, layout, i, j);
+}
+
+int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, int32_t* out_rows) {
+  if (P < 1 || P > RA_MAX_DEV || dev0 < 0 || dev0 >= P || n_local < 1 || dev0 + n_local > P || n < 0)
+    return RA_ERR_INVALID_ARG;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_ERR_INVALID_ARG;
+  if (!out_rows) return RA_ERR_INVALID_ARG;
+  const int64_t st = layout_stride(layout, P);
+  int32_t* row = out_rows;
+  for (int s = 0; s < P; ++s)
+    for (int i = dev0; i < dev0 + n_local; ++i) {
+      const int j = ((i - s) % P + P) % P;
+      row[0] = s;
+      row[1] = i;
+      row[2] = j;
+      row[3] = s & 1;
+      row[4] = classify(mask == RA_MASK_CAUSAL, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j),
+                        st, n);
+      row += 5;
+    }
+  return RA_OK;
+}
+
+int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, float* m, float* l, int n_dev, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale, int mask, const int64_t* q_off,
+                   int64_t q_stride, const int64_t* k_off, int64_t k_stride, int flags, void* stream) {
+  const Shape sh{n_dev, B, Hq, Hkv, Nq, Nk, D, dtype};
+  int rc = validate_shape(sh);
+  if (rc != RA_OK) return rc;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
+  if (flags & ~RA_STEP_INIT) return RA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
+  const bool causal = mask == RA_MASK_CAUSAL;
+  if (causal && (!q_off || !k_off || q_stride <= 0 || k_stride <= 0)) return RA_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  const size_t q_bytes = (size_t)n_dev * B * Nq * Hq * D * es;
+  const size_t kv_bytes = (size_t)n_dev * B * Nk * Hkv * D * es;
+  const size_t rows = (size_t)n_dev * B * Hq * Nq;
+  if (rows > 0 && (!q || !o_acc || !m || !l)) return RA_ERR_INVALID_ARG;
+  if (kv_bytes > 0 && (!k || !v)) return RA_ERR_INVALID_ARG;
+  // the state is written: it may not alias the inputs or itself
+  const void* outs[3] = {o_acc, m, l};
+  const size_t out_sz[3] = {rows * D * 4, rows * 4, rows * 4};
+  const void* ins[3] = {q, k, v};
+  const size_t in_sz[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 3; ++b)
+      if (overlaps(outs[a], out_sz[a], ins[b], in_sz[b])) return RA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return RA_ERR_INVALID_ARG;
+  }
+  if (rows == 0) return RA_OK;
+
+  StepParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_acc = o_acc;
+  p.m = m;
+  p.l = l;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.D = D;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = (float)(scale * kLog2e);
+  p.q_stride = causal ? q_stride : 1;
+  p.k_stride = causal ? k_stride : 1;
+  std::vector<int> skipped_init;
+  for (int t = 0; t < n_dev; ++t) {
+    const int64_t qo = q_off ? q_off[t] : 0, ko = k_off ? k_off[t] : 0;
+    const int cls = classify(causal, qo, p.q_stride, Nq, ko, p.k_stride, Nk);
+    if (cls == 0) {
+      if (flags & RA_STEP_INIT) skipped_init.push_back(t);
+      continue;
+    }
+    const int i = p.n_launch++;
+    p.slot[i] = t;
+    p.q_off[i] = qo;
+    p.k_off[i] = ko;
+    p.dflags[i] = (flags & RA_STEP_INIT) ? ra::kDevInit : 0;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (!skipped_init.empty()) {
+    rc = hip_status(ra::launch_init_state(o_acc, m, l, n_dev, skipped_init.data(), (int)skipped_init.size(), B, Hq,
+                                          Nq, D, st));
+    if (rc != RA_OK) return rc;
+  }
+  return hip_status(launch_step(p, dtype, st));
+}
+
+int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev, int B,
+                       int Hq, int Nq, int D, int out_dtype, void* stream) {
+  if (n_dev < 1 || n_dev > RA_MAX_DEV || B < 1 || Hq < 1 || Nq < 0 || D < 1) return RA_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return RA_ERR_INVALID_ARG;
+  if (D > RA_MAX_D) return RA_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)n_dev * B * Hq * Nq;
+  if (rows == 0) return RA_OK;
+  if (!o_acc || !m || !l || !o) return RA_ERR_INVALID_ARG;
+  const size_t o_bytes = rows * D * elem_size(out_dtype);
+  if (overlaps(o, o_bytes, o_acc, rows * D * 4) || overlaps(o, o_bytes, m, rows * 4) ||
+      overlaps(o, o_bytes, l, rows * 4) || overlaps(lse, rows * 4, o, o_bytes) ||
+      overlaps(lse, rows * 4, o_acc, rows * D * 4) || overlaps(lse, rows * 4, l, rows * 4))
+    return RA_ERR_INVALID_ARG;
+  return hip_status(ra::launch_finalize(o_acc, m, l, o, lse, n_dev, B, Hq, Nq, D, out_dtype, (hipStream_t)stream));
+}
+
+size_t ring_attn_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype) {
+  if (P < 1 || P > RA_MAX_DEV || n_local < 1 || n_local > P || B < 1 || Hq < 1 || Hkv < 1 || n < 0 || D < 1 ||
+      D > RA_MAX_D || Hq % Hkv || !valid_dtype(dtype))
+    return 0;
+  const size_t align = 256;
+  auto up = [&](size_t x) { return (x + align - 1) / align * align; };
+  const size_t blk = (size_t)B * n * Hkv * D * elem_size(dtype);
+  const size_t rows = (size_t)n_local * B * Hq * n;
+  return 4 * up((size_t)n_local * blk) + up(rows * D * 4) + 2 * up(rows * 4);
+}
+
+int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
+                    float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
+                    float scale, int mask, int layout, void* workspace, size_t workspace_bytes,
+                    void* compute_stream, void* copy_stream, void* const* step_events) {
+  if (P < 1 || P > RA_MAX_DEV || dev0 < 0 || dev0 >= P || n_local < 1 || dev0 + n_local > P) return RA_ERR_INVALID_ARG;
+  const Shape sh{n_local, B, Hq, Hkv, n, n, D, dtype};
+  int rc = validate_shape(sh);
+  if (rc != RA_OK) return rc;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
+  if (n == 0) return RA_OK;
+  if (!q_local || !k_src || !v_src || !o || !workspace) return RA_ERR_INVALID_ARG;
+  const size_t need = ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype);
+  if (need == 0) return RA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return RA_ERR_WORKSPACE;
+
+  const size_t es = elem_size(dtype);
+  const size_t blk = (size_t)B * n * Hkv * D * es;  // one device's K (or V) block
+  const size_t rows = (size_t)n_local * B * Hq * n;
+  const size_t q_bytes = rows * D * es;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* ws = (char*)workspace;
+  char* stage_k[2] = {ws, ws + up((size_t)n_local * blk)};
+  char* stage_v[2] = {ws + 2 * up((size_t)n_local * blk), ws + 3 * up((size_t)n_local * blk)};
+  float* o_acc = (float*)(ws + 4 * up((size_t)n_local * blk));
+  float* m_st = (float*)((char*)o_acc + up(rows * D * 4));
+  float* l_st = (float*)((char*)m_st + up(rows * 4));
+  // outputs may not alias inputs or the workspace
+  const size_t src_bytes = (size_t)P * blk;
+  const void* ro[4] = {q_local, kv_src_is_host ? nullptr : k_src, kv_src_is_host ? nullptr : v_src, workspace};
+  const size_t ro_sz[4] = {q_bytes, src_bytes, src_bytes, need};
+  for (int a = 0; a < 4; ++a)
+    if (overlaps(o, q_bytes, ro[a], ro_sz[a]) || overlaps(lse, rows * 4, ro[a], ro_sz[a])) return RA_ERR_INVALID_ARG;
+  if (overlaps(o, q_bytes, lse, rows * 4)) return RA_ERR_INVALID_ARG;
+  if (overlaps(workspace, need, q_local, q_bytes) ||
+      (!kv_src_is_host && (overlaps(workspace, need, k_src, src_bytes) || overlaps(workspace, need, v_src, src_bytes))))
+    return RA_ERR_INVALID_ARG;
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t xs = (hipStream_t)copy_stream;
+  const bool causal = mask == RA_MASK_CAUSAL;
+  const int64_t st = layout_stride(layout, P);
+
+  // per-device schedule: first and last computed step
+  std::vector<int> first_step(n_local, -1), last_step(n_local, -1);
+  std::vector<int> cls((size_t)P * n_local);
+  for (int s = 0; s < P; ++s)
+    for (int t = 0; t < n_local; ++t) {
+      const int i = dev0 + t;
+      const int j = ((i - s) % P + P) % P;
+      const int c = classify(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n);
+      cls[(size_t)s * n_local + t] = c;
+      if (c != 0) {
+        if (first_step[t] < 0) first_step[t] = s;
+        last_step[t] = s;
+      }
+    }
+
+  hipEvent_t ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr}, ev_fork = nullptr;
+  auto cleanup = [&]() {
+    for (int a = 0; a < 2; ++a) {
+      if (ev_copy[a]) (void)hipEventDestroy(ev_copy[a]);
+      if (ev_comp[a]) (void)hipEventDestroy(ev_comp[a]);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+  };
+#define RA_CHECK(x)            \
+  do {                         \
+    hipError_t e_ = (x);       \
+    if (e_ != hipSuccess) {    \
+      cleanup();               \
+      return RA_ERR_HIP;       \
+    }                          \
+  } while (0)
+
+  for (int a = 0; a < 2; ++a) {
+    RA_CHECK(hipEventCreateWithFlags(&ev_copy[a], hipEventDisableTiming));
+    RA_CHECK(hipEventCreateWithFlags(&ev_comp[a], hipEventDisableTiming));
+  }
+  RA_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
+  const bool two_streams = xs != cs;
+  if (two_streams) {
+    RA_CHECK(hipEventRecord(ev_fork, cs));
+    RA_CHECK(hipStreamWaitEvent(xs, ev_fork, 0));
+  }
+  const hipMemcpyKind kind = kv_src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+  const char* ksrc = (const char*)k_src;
+  const char* vsrc = (const char*)v_src;
+
+  // copies that bring the blocks of step s into staging slot s & 1
+  auto enqueue_hop = [&](int s) -> hipError_t {
+    const int sl = s & 1;
+    hipError_t e;
+    if (kv_src_is_host || s == 0) {
+      // every device receives block (i - s) mod P from the source (pinned host memory here)
+      for (int t = 0; t < n_local; ++t) {
+        const int j = ((dev0 + t - s) % P + P) % P;
+        if ((e = hipMemcpyAsync(stage_k[sl] + t * blk, ksrc + j * blk, blk, kind, xs)) != hipSuccess) return e;
+        if ((e = hipMemcpyAsync(stage_v[sl] + t * blk, vsrc + j * blk, blk, kind, xs)) != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+    // device i receives what device i-1 held in step s-1
+    const char* prev_k = (s == 1) ? ksrc + (size_t)dev0 * blk : stage_k[sl ^ 1];
+    const char* prev_v = (s == 1) ? vsrc + (size_t)dev0 * blk : stage_v[sl ^ 1];
+    if (n_local > 1) {
+      if ((e = hipMemcpyAsync(stage_k[sl] + blk, prev_k, (n_local - 1) * blk, hipMemcpyDeviceToDevice, xs)) !=
+          hipSuccess)
+        return e;
+      if ((e = hipMemcpyAsync(stage_v[sl] + blk, prev_v, (n_local - 1) * blk, hipMemcpyDeviceToDevice, xs)) !=
+          hipSuccess)
+        return e;
+    }
+    // device dev0: its predecessor is local only when the whole ring is local
+    const char* k0;
+    const char* v0;
+    if (n_local == P) {
+      k0 = prev_k + (size_t)(n_local - 1) * blk;
+      v0 = prev_v + (size_t)(n_local - 1) * blk;
+    } else {
+      const int j = ((dev0 - s) % P + P) % P;  // block arriving from the (remote) predecessor
+      k0 = ksrc + (size_t)j * blk;
+      v0 = vsrc + (size_t)j * blk;
+    }
+    if ((e = hipMemcpyAsync(stage_k[sl], k0, blk, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
+    return hipMemcpyAsync(stage_v[sl], v0, blk, hipMemcpyDeviceToDevice, xs);
+  };
+
+  if (kv_src_is_host) {
+    RA_CHECK(enqueue_hop(0));
+    RA_CHECK(hipEventRecord(ev_copy[0], xs));
+  }
+  for (int s = 0; s < P; ++s) {
+    // hop for step s+1, into the slot that step s-1 read
+    if (s + 1 < P) {
+      if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
+      RA_CHECK(enqueue_hop(s + 1));
+      RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
+    }
+    const bool staged = kv_src_is_host || s > 0;
+    if (staged) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
+
+    StepParams p{};
+    p.q = q_local;
+    p.k = staged ? (const void*)stage_k[s & 1] : (const void*)(ksrc + (size_t)dev0 * blk);
+    p.v = staged ? (const void*)stage_v[s & 1] : (const void*)(vsrc + (size_t)dev0 * blk);
+    p.o_acc = o_acc;
+    p.m = m_st;
+    p.l = l_st;
+    p.o_out = o;
+    p.lse_out = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = n;
+    p.Nk = n;
+    p.D = D;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = (float)(scale * kLog2e);
+    p.q_stride = st;
+    p.k_stride = st;
+    for (int t = 0; t < n_local; ++t) {
+      if (cls[(size_t)s * n_local + t] == 0) continue;
+      const int i = dev0 + t;
+      const int j = ((i - s) % P + P) % P;
+      const int x = p.n_launch++;
+      p.slot[x] = t;
+      p.q_off[x] = block_offset(layout, P, n, i);
+      p.k_off[x] = block_offset(layout, P, n, j);
+      p.dflags[x] = (s == first_step[t] ? ra::kDevInit : 0) | (s == last_step[t] ? ra::kDevFinal : 0);
+    }
+    if (step_events) RA_CHECK(hipEventRecord((hipEvent_t)step_events[2 * s], cs));
+    RA_CHECK(launch_step(p, dtype, cs));
+    if (step_events) RA_CHECK(hipEventRecord((hipEvent_t)step_events[2 * s + 1], cs));
+    RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+  }
+  // devices that never computed (no visible block): empty output
+  for (int t = 0; t < n_local; ++t)
+    if (first_step[t] < 0) {
+      int slot_t = t;
+      RA_CHECK(ra::launch_init_state(o_acc, m_st, l_st, n_local, &slot_t, 1, B, Hq, n, D, cs));
+      const size_t per = (size_t)B * Hq * n;
+      RA_CHECK(ra::launch_finalize(o_acc + t * per * D, m_st + t * per, l_st + t * per, (char*)o + t * per * D * es,
+                                   lse ? lse + t * per : nullptr, 1, B, Hq, n, D, dtype, cs));
+    }
+  // join: both streams ordered after all work of this call
+  if (two_streams) {
+    RA_CHECK(hipEventRecord(ev_copy[0], xs));
+    RA_CHECK(hipStreamWaitEvent(cs, ev_copy[0], 0));
+    RA_CHECK(hipEventRecord(ev_comp[0], cs));
+    RA_CHECK(hipStreamWaitEvent(xs, ev_comp[0], 0));
+  }
+  cleanup();
+#undef RA_CHECK
+  return RA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Shared host/device definitions of the ring-attention HIP library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ring_attn.h"
+
+namespace ra {
+
+// Per-device flags inside one step launch.
+enum : uint8_t {
+  kDevInit = 1,   // ignore incoming state (first block folded by this device)
+  kDevFinal = 2,  // last block of this device: write o = o_acc / l and lse instead of the state
+};
+
+// Everything one step launch needs.  Passed by value as the kernel argument (about 1.5 KiB).
+// Device t of the launch (0 <= t < n_launch) addresses q, k, v, state and outputs at index slot[t]
+// of their leading [n_dev] dimension.
+struct StepParams {
+  const void* q;     // [n_dev, B, Nq, Hq, D]
+  const void* k;     // [n_dev, B, Nk, Hkv, D]
+  const void* v;     // [n_dev, B, Nk, Hkv, D]
+  float* o_acc;      // [n_dev, B, Hq, Nq, D]
+  float* m;          // [n_dev, B, Hq, Nq]
+  float* l;          // [n_dev, B, Hq, Nq]
+  void* o_out;       // [n_dev, B, Nq, Hq, D] (devices with kDevFinal)
+  float* lse_out;    // [n_dev, B, Hq, Nq] or null
+  int n_launch;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal;
+  float scale_log2;  // scale * log2(e)
+  int64_t q_stride, k_stride;
+  // XCD-aware work decomposition (bf16 MFMA kernel): groups = n_launch * B * Hkv
+  int groups, groups_per_xcd, n_qtiles;
+  int slot[RA_MAX_DEV];
+  int64_t q_off[RA_MAX_DEV];
+  int64_t k_off[RA_MAX_DEV];
+  uint8_t dflags[RA_MAX_DEV];
+};
+
+// Launchers (defined in the kernel sources); return a hipError_t.
+hipError_t launch_step_mfma_bf16_d128(const StepParams& p, hipStream_t stream);
+hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream);
+hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
+                           int B, int Hq, int Nq, int D, int out_dtype, hipStream_t stream);
+hipError_t launch_init_state(float* o_acc, float* m, float* l, int n_dev_total, const int* slots, int n_slots,
+                             int B, int Hq, int Nq, int D, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,209 @@
+// Generic ring-attention step kernel (fp32 arithmetic; fp32 or bf16 storage; any head dim <= 128),
+// plus the finalize and state-initialisation kernels.
+//
+// The generic step is the straightforward form of the per-step fold on the Ultralytics glossary
+// page "Ring Attention", section "Como funciona a atenção em anel", with the exact running maximum
+// of "Sequence Parallelism and Ring Attention", section "Approfondimento tecnico": keys are taken
+// one at a time, the state is rescaled whenever a key raises the maximum.  It serves the fp32 path,
+// head dims other than 128 and small shapes; the bf16 head-dim-128 hot path has its own MFMA kernel.
+//
+// Layout: 16 lanes cooperate on one query row (lane `sub` owns dims sub, sub+16, ...), 16 rows per
+// 256-thread workgroup; the dot product is reduced across the 16 lanes with xor shuffles.
+#include "internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int kLanesPerRow = 16;
+constexpr int kRowsPerBlock = 16;
+constexpr int kMaxPerLane = RA_MAX_D / kLanesPerRow;  // 8
+constexpr float kLn2 = 0.693147180559945309f;
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, size_t i) {
+  if constexpr (BF16) {
+    const unsigned short b = ((const unsigned short*)base)[i];
+    return __uint_as_float((unsigned)b << 16);
+  } else {
+    return ((const float*)base)[i];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* base, size_t i, float x) {
+  if constexpr (BF16) {
+    ((unsigned short*)base)[i] = __builtin_bit_cast(unsigned short, (__bf16)x);
+  } else {
+    ((float*)base)[i] = x;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void step_generic(const StepParams p) {
+  const int sub = threadIdx.x % kLanesPerRow;
+  const int qr = blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int h = blockIdx.y;
+  const int dl = blockIdx.z / p.B;
+  const int bb = blockIdx.z % p.B;
+  if (qr >= p.Nq) return;  // whole 16-lane groups leave together
+  const int D = p.D, Nq = p.Nq, Nk = p.Nk, Hq = p.Hq, Hkv = p.Hkv;
+  const int dev = p.slot[dl];
+  const int dfl = p.dflags[dl];
+  const int kvh = h / (Hq / Hkv);
+
+  float q[kMaxPerLane], o[kMaxPerLane];
+  const size_t qoff = (((size_t)dev * p.B + bb) * Nq + qr) * Hq * D + (size_t)h * D;
+#pragma unroll
+  for (int e = 0; e < kMaxPerLane; ++e) {
+    const int d = sub + kLanesPerRow * e;
+    q[e] = d < D ? load_elem<BF16>(p.q, qoff + d) : 0.f;
+    o[e] = 0.f;
+  }
+
+  int kmax = Nk - 1;
+  if (p.causal) {
+    const int64_t dpos = p.q_off[dl] + (int64_t)qr * p.q_stride - p.k_off[dl];
+    if (dpos < 0) {
+      kmax = -1;
+    } else {
+      const int64_t kk = dpos / p.k_stride;
+      kmax = kk < (int64_t)(Nk - 1) ? (int)kk : Nk - 1;
+    }
+  }
+
+  const float c = p.scale_log2;
+  float M = -INFINITY, l = 0.f;
+  const size_t kvrow = (size_t)Hkv * D;
+  const size_t kvbase = ((size_t)dev * p.B + bb) * Nk * kvrow + (size_t)kvh * D;
+  for (int u = 0; u <= kmax; ++u) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      const int d = sub + kLanesPerRow * e;
+      if (d < D) part = __builtin_fmaf(q[e], load_elem<BF16>(p.k, kvbase + u * kvrow + d), part);
+    }
+#pragma unroll
+    for (int w = kLanesPerRow / 2; w >= 1; w /= 2) part += __shfl_xor(part, w, kLanesPerRow);
+    const float x = part * c;
+    if (x > M) {
+      const float alpha = exp2f(M - x);  // 0 when M = -inf
+#pragma unroll
+      for (int e = 0; e < kMaxPerLane; ++e) o[e] *= alpha;
+      l *= alpha;
+      M = x;
+    }
+    const float pr = exp2f(x - M);
+    l += pr;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      const int d = sub + kLanesPerRow * e;
+      if (d < D) o[e] = __builtin_fmaf(pr, load_elem<BF16>(p.v, kvbase + u * kvrow + d), o[e]);
+    }
+  }
+
+  // merge with the incoming state
+  const size_t srow = (((size_t)dev * p.B + bb) * Hq + h) * Nq + qr;
+  const bool has_old = !(dfl & kDevInit);
+  const float Mo = has_old ? p.m[srow] : -INFINITY;
+  const float lo = has_old ? p.l[srow] : 0.f;
+  const float Mf = fmaxf(Mo, M);
+  const float ao = Mo == -INFINITY ? 0.f : exp2f(Mo - Mf);
+  const float an = M == -INFINITY ? 0.f : exp2f(M - Mf);
+  const float lf = ao * lo + an * l;
+  float* oacc = p.o_acc + srow * D;
+  if (dfl & kDevFinal) {
+    const float inv = lf > 0.f ? 1.0f / lf : 0.f;
+    const size_t ooff = (((size_t)dev * p.B + bb) * Nq + qr) * Hq * D + (size_t)h * D;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      const int d = sub + kLanesPerRow * e;
+      if (d < D) store_elem<BF16>(p.o_out, ooff + d, (ao * (has_old ? oacc[d] : 0.f) + an * o[e]) * inv);
+    }
+    if (sub == 0 && p.lse_out) p.lse_out[srow] = lf > 0.f ? (Mf + log2f(lf)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      const int d = sub + kLanesPerRow * e;
+      if (d < D) oacc[d] = ao * (has_old ? oacc[d] : 0.f) + an * o[e];
+    }
+    if (sub == 0) {
+      p.m[srow] = Mf;
+      p.l[srow] = lf;
+    }
+  }
+}
+
+// o[dev, b, t, h, :] = o_acc[dev, b, h, t, :] / l ; lse = ln2 * (m + log2 l).  One thread per output element.
+template <bool BF16>
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ o_acc, const float* __restrict__ m,
+                                                       const float* __restrict__ l, void* __restrict__ o,
+                                                       float* __restrict__ lse, int B, int Hq, int Nq, int D,
+                                                       size_t total) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int d = (int)(i % D);
+  size_t r = i / D;
+  const int h = (int)(r % Hq);
+  r /= Hq;
+  const int t = (int)(r % Nq);
+  const size_t db = r / Nq;  // dev * B + b
+  const size_t srow = (db * Hq + h) * Nq + t;
+  const float lv = l[srow];
+  const float val = lv > 0.f ? o_acc[srow * D + d] / lv : 0.f;
+  store_elem<BF16>(o, i, val);
+  if (d == 0 && lse) lse[srow] = lv > 0.f ? (m[srow] + log2f(lv)) * kLn2 : -INFINITY;
+}
+
+// Empty state (m = -inf, l = 0, o_acc = 0) for the listed device slots.
+__global__ __launch_bounds__(256) void init_state_kernel(float* o_acc, float* m, float* l, int slot, size_t rows,
+                                                         int D) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t base = (size_t)slot * rows;
+  if (i < rows) {
+    m[base + i] = -INFINITY;
+    l[base + i] = 0.f;
+  }
+  if (i < rows * D) o_acc[base * D + i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream) {
+  if (p.Nq == 0 || p.n_launch == 0) return hipSuccess;
+  dim3 grid((p.Nq + kRowsPerBlock - 1) / kRowsPerBlock, p.Hq, p.n_launch * p.B);
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(step_generic<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(step_generic<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev, int B,
+                           int Hq, int Nq, int D, int out_dtype, hipStream_t stream) {
+  const size_t total = (size_t)n_dev * B * Nq * Hq * D;
+  if (total == 0) return hipSuccess;
+  const size_t blocks = (total + 255) / 256;
+  if (out_dtype == RA_BF16)
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, o_acc, m, l, o, lse, B, Hq,
+                       Nq, D, total);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, o_acc, m, l, o, lse, B,
+                       Hq, Nq, D, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_state(float* o_acc, float* m, float* l, int /*n_dev_total*/, const int* slots, int n_slots,
+                             int B, int Hq, int Nq, int D, hipStream_t stream) {
+  const size_t rows = (size_t)B * Hq * Nq;
+  if (rows == 0) return hipSuccess;
+  const size_t blocks = (rows * D + 255) / 256;
+  for (int i = 0; i < n_slots; ++i) {
+    hipLaunchKernelGGL(init_state_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o_acc, m, l, slots[i], rows,
+                       D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace ra

@@ -1,0 +1,170 @@
+/*
+ * ring_attn.h — C ABI of the per-device hot path of blockwise ring attention on MI355X (gfx950).
+ *
+ * The method (sources are cited by page title and section):
+ *   - Ultralytics glossary, "Ring Attention", section "Como funciona a atenção em anel": a sequence
+ *     is split into N blocks, one per device.  Each device keeps its query block for the whole
+ *     computation; in each of N steps it computes attention between its queries and the key/value
+ *     block it holds, sends that block to the next device and receives one from the previous device.
+ *     Partial results are combined with the accumulated softmax of flash attention: a running sum of
+ *     exponentiated scores and of score-weighted values, divided one by the other at the end.  The
+ *     same section notes that production kernels subtract a running maximum before exponentiating,
+ *     that a causal mask leaves the devices holding the first query blocks mostly idle, and that
+ *     Striped Attention evens this out by spreading the tokens uniformly over the devices.
+ *   - "Sequence Parallelism and Ring Attention" (aiunderstanding.org), section "Approfondimento
+ *     tecnico": online softmax keeps a running maximum and normaliser and rescales earlier partial
+ *     sums when a larger value appears, so the blockwise result equals full attention.
+ *   - "Ring Attention Là Gì?" (thienlv.com), section "Ring Attention Hoạt Động Thế Nào?": while a
+ *     device computes with the current block it is already sending the next one.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, except where marked "host".
+ *     The caller keeps them alive until the work enqueued on the given stream(s) has completed.
+ *   - `stream` arguments are hipStream_t values passed as void* (NULL = the default stream).
+ *     Every call only enqueues work and returns; kernel faults surface at the caller's
+ *     synchronisation.  Launch failures are reported as RA_ERR_HIP.
+ *   - Every call returns RA_OK (0) or a negative RA_ERR_* code.  Arguments are validated before any
+ *     HIP call, so validation errors are reported without touching the GPU.  No C++ exception
+ *     crosses this boundary.
+ *   - bf16 tensors hold raw bfloat16 bit patterns (uint16).  Shapes are row-major, last index fastest.
+ *   - Token positions: local row r of device t has global position  off[t] + r * stride.  With
+ *     contiguous sharding off[t] = t*n, stride = 1; with striped sharding (token p on shard p mod P)
+ *     off[t] = t, stride = P.  Under RA_MASK_CAUSAL key u is visible to query t iff pos(u) <= pos(t).
+ *   - Grouped-query attention: query head h reads key/value head h / (Hq / Hkv).
+ *
+ * Running state between ring steps (fp32, caller-owned, persistent across calls):
+ *   o_acc[dev, b, h, t, :] = sum_u 2^(x_u - m[dev,b,h,t]) * v_u
+ *   l[dev, b, h, t]        = sum_u 2^(x_u - m[dev,b,h,t])
+ *   where x_u = log2(e) * scale * <q_t, k_u> over the visible keys folded so far, and m is a
+ *   reference exponent (the running maximum of x, possibly lagging it by at most 8), or -inf while
+ *   no visible key has been folded (then o_acc = 0 and l = 0).
+ *   Shapes: o_acc [n_dev, B, Hq, Nq, D], m and l [n_dev, B, Hq, Nq].
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define RA_F32 0  /* float32 */
+#define RA_BF16 1 /* bfloat16 bit patterns */
+
+/* mask modes */
+#define RA_MASK_NONE 0
+#define RA_MASK_CAUSAL 1
+
+/* token layouts (ring_attn_local, ring_attn_plan) */
+#define RA_LAYOUT_CONTIGUOUS 0
+#define RA_LAYOUT_STRIPED 1
+
+/* status codes */
+#define RA_OK 0
+#define RA_ERR_INVALID_ARG (-1) /* null pointer, bad size, inconsistent shape, overlapping buffers */
+#define RA_ERR_UNSUPPORTED (-2) /* valid but not implemented (e.g. head dim > 128) */
+#define RA_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
+#define RA_ERR_WORKSPACE (-4)   /* workspace too small */
+
+/* ring_attn_step flags */
+#define RA_STEP_INIT 1 /* ignore the incoming state: treat it as m = -inf, l = 0, o_acc = 0 */
+
+#define RA_MAX_DEV 64 /* largest ring size / number of devices batched into one call */
+#define RA_MAX_D 128  /* largest head dimension */
+
+/*
+ * ring_attn_step — fold one key/value block into the running online-softmax state of a query
+ * block, for n_dev independent (query block, key/value block) pairs at once (n_dev = 1 for one
+ * device; n_dev = P to process one ring step of P emulated devices in a single launch).
+ * Defining passage: the per-step attention and accumulation of the Ultralytics "Ring Attention"
+ * page, section "Como funciona a atenção em anel", with the running-maximum rescaling of
+ * "Sequence Parallelism and Ring Attention", section "Approfondimento tecnico".
+ *
+ *   q      [n_dev, B, Nq, Hq, D]  (dtype)      query block of each device (read only)
+ *   k, v   [n_dev, B, Nk, Hkv, D] (dtype)      the key/value block each device holds (read only)
+ *   o_acc, m, l                                running state (read unless RA_STEP_INIT, written)
+ *   scale                                      multiplies q.k (pass 1/sqrt(D))
+ *   mask                                       RA_MASK_NONE or RA_MASK_CAUSAL
+ *   q_off, k_off  host int64[n_dev]            position offsets (may be NULL when mask is NONE)
+ *   q_stride, k_stride                         position strides (> 0 under RA_MASK_CAUSAL)
+ *   flags                                      RA_STEP_INIT or 0
+ * Key/value blocks that are fully masked for a device (min key position > max query position)
+ * are skipped without a launch; the state of that device is left as it was (or initialised to
+ * the empty state under RA_STEP_INIT).  Supported: 1 <= D <= 128; bf16 with D == 128 runs the
+ * MFMA kernel, every other case the generic fp32-arithmetic kernel.  Nq or Nk may be 0.
+ */
+int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, float* m, float* l,
+                   int n_dev, int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
+                   int mask, const int64_t* q_off, int64_t q_stride, const int64_t* k_off,
+                   int64_t k_stride, int flags, void* stream);
+
+/*
+ * ring_attn_finalize — divide the accumulated numerator by the denominator after the last block
+ * and produce the log-sum-exp (Ultralytics "Ring Attention", "Como funciona a atenção em anel":
+ * the division happens once, at the end).
+ *   o   [n_dev, B, Nq, Hq, D] (out_dtype)  o = o_acc / l, written in token-major layout
+ *   lse [n_dev, B, Hq, Nq] fp32 (may be NULL)  natural log of sum_u exp(scale * <q_t, k_u>)
+ * Rows with l == 0 (no visible key) get o = 0 and lse = -inf.
+ */
+int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
+                       int B, int Hq, int Nq, int D, int out_dtype, void* stream);
+
+/*
+ * ring_attn_local — the whole ring schedule for the devices [dev0, dev0 + n_local) of a P-way
+ * ring, run on this GPU (Ultralytics "Ring Attention", "Como funciona a atenção em anel": P steps;
+ * in step s device i holds block (i - s) mod P, received from device i - 1; "Ring Attention Là
+ * Gì?", "Ring Attention Hoạt Động Thế Nào?": the next block is in flight during compute).
+ *
+ *   q_local [n_local, B, n, Hq, D]   queries of the local devices, in shard order (dtype)
+ *   k_src, v_src [P, B, n, Hkv, D]   every shard's keys/values in shard order (dtype); device
+ *                                    memory, or pinned host memory when kv_src_is_host != 0
+ *   o   [n_local, B, n, Hq, D]       output (dtype), token-major, in shard order
+ *   lse [n_local, B, Hq, n] fp32     log-sum-exp (may be NULL)
+ *   layout                           RA_LAYOUT_CONTIGUOUS or RA_LAYOUT_STRIPED (sets positions)
+ *   workspace                        device buffer of >= ring_attn_local_workspace_bytes(...) bytes:
+ *                                    two staging slots of K and V for the local devices, and the
+ *                                    fp32 running state
+ *   compute_stream, copy_stream      hipStream_t; the hops run on copy_stream, double-buffered
+ *                                    against the step kernels on compute_stream (they may be equal)
+ *   step_events  (may be NULL)       host array of 2*P hipEvent_t handles created by the caller;
+ *                                    events 2s and 2s+1 are recorded on compute_stream around the
+ *                                    step-s kernel (for timing)
+ * Hops: a local device whose ring predecessor is also local receives the block its predecessor
+ * held (a copy from that device's staging slot); otherwise the block is copied from k_src/v_src.
+ * With a device-resident source a device's own block (step 0) is read in place.  Under
+ * RA_MASK_CAUSAL, fully masked blocks are still passed on but not computed.  The last step of
+ * each device writes o and lse directly.  The call returns after enqueueing; both streams are
+ * left ordered after all of its work.
+ */
+int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
+                    float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
+                    float scale, int mask, int layout, void* workspace, size_t workspace_bytes,
+                    void* compute_stream, void* copy_stream, void* const* step_events);
+
+/* Workspace size in bytes for ring_attn_local with these arguments (0 on invalid arguments). */
+size_t ring_attn_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype);
+
+/*
+ * ring_attn_plan — the ring schedule as a table, computed on the host (no HIP call).
+ * For each step s in [0, P) and each local device i in [dev0, dev0 + n_local), one row of 5 int32:
+ *   { s, i, j = (i - s) mod P, staging slot (s mod 2), class }
+ * class: 0 = fully masked (skipped), 1 = fully visible, 2 = partially visible (masked tiles).
+ * out_rows (host) must hold P * n_local * 5 int32.
+ */
+int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, int32_t* out_rows);
+
+/* Visible (query, key) pairs between query block i and key block j of a P-way ring with n tokens
+ * per block under the given mask and layout (host arithmetic; -1 on invalid arguments). */
+int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j);
+
+/* Human-readable text for a status code (static storage). */
+const char* ring_attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

@@ -1,0 +1,257 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI (small and ragged shapes).
+
+Tolerances: fp32 inputs, max abs 1e-5; bf16 inputs with fp32 accumulation, output max abs 2e-2 and
+log-sum-exp max abs 1e-3.  Shapes span several 128-row query tiles and 64-key tiles plus a ragged
+tail, in both layouts, with and without the causal mask, with grouped-query heads.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from ring_harness import (TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_err, out_to_f64, run_ring_local, shard, to_device,
+                          to_float, unshard_lse, unshard_out)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, S, Hq, Hkv, D, seed, dtype, sigma=1.0):
+    gen = si.normal_bf16 if dtype == "bf16" else si.normal_f32
+    return (gen(seed, (B, S, Hq, D), sigma), gen(seed + 1, (B, S, Hkv, D), sigma), gen(seed + 2, (B, S, Hkv, D), sigma))
+
+
+def _check_ring(gpu_lib, B, P, n, Hq, Hkv, D, causal, layout, dtype, seed, sigma=1.0, host_kv=False, two_streams=True):
+    S = P * n
+    q, k, v = _inputs(B, S, Hq, Hkv, D, seed, dtype, sigma)
+    o, lse = run_ring_local(q, k, v, P=P, causal=causal, layout=layout, dtype=dtype, host_kv=host_kv,
+                            two_streams=two_streams)
+    ref_o, ref_lse = oracle.attention_reference(to_float(q, dtype), to_float(k, dtype), to_float(v, dtype),
+                                                causal=causal)
+    eo = max_err(unshard_out(o, layout), ref_o)
+    el = max_err(unshard_lse(lse, layout), ref_lse)
+    print(f"[parity] B={B} P={P} n={n} Hq={Hq} Hkv={Hkv} D={D} causal={causal} {layout} {dtype}: "
+          f"max|dO|={eo:.3g} max|dLSE|={el:.3g}", flush=True)
+    if dtype == "f32":
+        assert eo <= TOL_F32 and el <= TOL_F32
+    else:
+        assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    return eo, el
+
+
+def test_demo_four_devices_fp32(gpu_lib):
+    """The pages' demonstration: 4 devices x 8 tokens, d=16, seed 0, fp32, no mask."""
+    q, k, v = si.demo_qkv()
+    q, k, v = (x.reshape(1, 32, 1, 16) for x in (q, k, v))
+    o, lse = run_ring_local(q, k, v, P=4, causal=False, layout="contiguous", dtype="f32", scale=0.25)
+    ref_o, ref_lse = oracle.attention_reference(q, k, v, scale=0.25)
+    assert max_err(unshard_out(o, "contiguous"), ref_o) <= TOL_F32
+    assert max_err(unshard_lse(lse, "contiguous"), ref_lse) <= TOL_F32
+    # and against the library softmax the demonstration compares with
+    full = torch.softmax(torch.from_numpy(q[0, :, 0]) @ torch.from_numpy(k[0, :, 0]).T / 4.0, dim=-1) @ torch.from_numpy(
+        v[0, :, 0])
+    assert torch.allclose(torch.from_numpy(unshard_out(o, "contiguous")[0, :, 0]).float(), full, atol=1e-5)
+
+
+@pytest.mark.parametrize("causal,layout", [(False, "contiguous"), (True, "contiguous"), (True, "striped")])
+@pytest.mark.parametrize("D", [16, 40, 64, 128])
+def test_fp32_ring(gpu_lib, causal, layout, D):
+    _check_ring(gpu_lib, 1, 4, 37, 3, 1, D, causal, layout, "f32", 100 + D)
+
+
+@pytest.mark.parametrize("causal,layout", [(False, "contiguous"), (True, "contiguous"), (True, "striped")])
+@pytest.mark.parametrize("n", [128, 200, 320])
+def test_bf16_mfma_ring(gpu_lib, causal, layout, n):
+    _check_ring(gpu_lib, 2, 4, n, 4, 2, 128, causal, layout, "bf16", 200 + n)
+
+
+def test_bf16_mfma_ring_gqa_striped_p8(gpu_lib):
+    _check_ring(gpu_lib, 1, 8, 192, 8, 2, 128, True, "striped", "bf16", 300)
+
+
+def test_bf16_generic_head_dim_64(gpu_lib):
+    _check_ring(gpu_lib, 1, 4, 96, 4, 4, 64, True, "contiguous", "bf16", 400)
+
+
+def test_single_stream_and_host_source(gpu_lib):
+    _check_ring(gpu_lib, 1, 4, 160, 4, 1, 128, True, "contiguous", "bf16", 500, two_streams=False)
+    _check_ring(gpu_lib, 1, 4, 160, 4, 1, 128, True, "striped", "bf16", 501, host_kv=True)
+    _check_ring(gpu_lib, 1, 4, 40, 2, 1, 32, False, "contiguous", "f32", 502, host_kv=True)
+
+
+def test_one_device_share_of_a_longer_ring(gpu_lib):
+    """Only the last device of an 8-way causal ring runs locally (dev0 = 7, n_local = 1)."""
+    P, n, Hq, Hkv, D = 8, 192, 4, 4, 128
+    S = P * n
+    q, k, v = _inputs(1, S, Hq, Hkv, D, 600, "bf16")
+    o, lse = run_ring_local(q[:, (P - 1) * n:], k, v, P=P, causal=True, layout="contiguous", dtype="bf16", dev0=P - 1,
+                            n_local=1)
+    rows = np.array([[0, h, t] for h in range(Hq) for t in range((P - 1) * n, S)])
+    ref_o, ref_lse = oracle.attention_rows(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"), rows,
+                                           causal=True)
+    got_o = o[0, 0].transpose(1, 0, 2).reshape(-1, D)
+    got_lse = lse[0, 0].reshape(-1)
+    assert max_err(got_o, ref_o) <= TOL_BF16_O and max_err(got_lse, ref_lse) <= TOL_BF16_LSE
+
+
+def test_large_scores_stay_finite(gpu_lib):
+    """Scores far beyond exp's fp32 range (queries scaled by 30, max score > 88.7): the running
+    maximum keeps everything finite and the result exact; values stay N(0, 1)."""
+    for dtype, D in (("bf16", 128), ("f32", 32)):
+        P, n, H = 4, 130, 2
+        S = P * n
+        q, k, v = _inputs(1, S, H, H, D, 700 + D, dtype)
+        qf = to_float(q, dtype) * 30.0
+        q = si.bf16_bits(qf) if dtype == "bf16" else qf.astype(np.float32)
+        scores = np.einsum("shd,thd->hst", to_float(q, dtype)[0], to_float(k, dtype)[0]) / math.sqrt(D)
+        assert scores.max() > 88.7
+        o, lse = run_ring_local(q, k, v, P=P, causal=True, layout="contiguous", dtype=dtype)
+        ref_o, ref_lse = oracle.attention_reference(to_float(q, dtype), to_float(k, dtype), to_float(v, dtype),
+                                                    causal=True)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        # fp32 bound at these magnitudes: a score near 150 carries fp32 spacing ~1.5e-5 and its D-term
+        # dot product about sqrt(D) such roundings, which shifts the weights by that relative amount;
+        # the output moves by at most that times max|v|, and the LSE by that plus 2 ulps of |LSE|
+        score_err = math.sqrt(D) * 2.0 ** -23 * np.abs(scores).max()
+        lse_ulps = 2 * 2.0 ** -23 * np.abs(ref_lse).max()
+        vmax = np.abs(to_float(v, dtype)).max()
+        tol_o, tol_l = ((TOL_BF16_O, TOL_BF16_LSE) if dtype == "bf16"
+                        else (TOL_F32 + score_err * vmax, TOL_F32 + score_err + lse_ulps))
+        assert max_err(unshard_out(o, "contiguous"), ref_o) <= tol_o
+        assert max_err(unshard_lse(lse, "contiguous"), ref_lse) <= tol_l
+
+
+# ---------------------------------------------------------------- ring_attn_step used directly
+
+def _state(n_dev, B, Hq, Nq, D):
+    return (torch.zeros((n_dev, B, Hq, Nq, D), dtype=torch.float32, device="cuda"),
+            torch.zeros((n_dev, B, Hq, Nq), dtype=torch.float32, device="cuda"),
+            torch.zeros((n_dev, B, Hq, Nq), dtype=torch.float32, device="cuda"))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 48)])
+def test_arrival_order_does_not_matter(gpu_lib, dtype, D):
+    """Each device folds the ring's blocks in a random order (one ring_attn_step per block)."""
+    ra = gpu_lib
+    P, n, Hq, Hkv = 4, 144, 2, 1
+    S = P * n
+    q, k, v = _inputs(1, S, Hq, Hkv, D, 800 + D, dtype)
+    ref_o, ref_lse = oracle.attention_reference(to_float(q, dtype), to_float(k, dtype), to_float(v, dtype), causal=True)
+    layout = "striped"
+    qs, ks, vs = shard(q, P, layout), shard(k, P, layout), shard(v, P, layout)
+    rng = np.random.default_rng(801)
+    o_acc, m, l = _state(P, 1, Hq, n, D)
+    tq = to_device(qs, dtype)
+    tk = [to_device(np.ascontiguousarray(ks[j:j + 1]), dtype) for j in range(P)]
+    tv = [to_device(np.ascontiguousarray(vs[j:j + 1]), dtype) for j in range(P)]
+    orders = [rng.permutation(P) for _ in range(P)]
+    for i in range(P):
+        qi = tq[i:i + 1].contiguous()
+        st = [x[i:i + 1].contiguous() for x in (o_acc, m, l)]
+        for step, j in enumerate(orders[i]):
+            ra.ring_attn_step(qi, tk[j], tv[j], *st, scale=1 / math.sqrt(D), causal=True, q_off=[i], q_stride=P,
+                              k_off=[int(j)], k_stride=P, init=(step == 0))
+        for x, y in zip((o_acc, m, l), st):
+            x[i:i + 1].copy_(y)
+    o = torch.empty_like(tq)
+    lse = torch.empty((P, 1, Hq, n), dtype=torch.float32, device="cuda")
+    ra.ring_attn_finalize(o_acc, m, l, o, lse)
+    torch.cuda.synchronize()
+    eo = max_err(unshard_out(out_to_f64(o), layout), ref_o)
+    el = max_err(unshard_lse(lse.cpu().numpy(), layout), ref_lse)
+    tol_o, tol_l = (TOL_BF16_O, TOL_BF16_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    assert eo <= tol_o and el <= tol_l
+
+
+def test_splitting_a_block_gives_the_same_state(gpu_lib):
+    """Folding a block in two halves equals folding it at once (the merge is associative)."""
+    ra = gpu_lib
+    n, Hq, D = 256, 2, 128
+    q, k, v = _inputs(1, n, Hq, Hq, D, 900, "bf16")
+    tq, tk, tv = to_device(q[None], "bf16"), to_device(k[None], "bf16"), to_device(v[None], "bf16")
+    whole = _state(1, 1, Hq, n, D)
+    ra.ring_attn_step(tq, tk, tv, *whole, scale=D ** -0.5, init=True)
+    halves = _state(1, 1, Hq, n, D)
+    h = n // 2 + 64
+    ra.ring_attn_step(tq, tk[:, :, :h].contiguous(), tv[:, :, :h].contiguous(), *halves, scale=D ** -0.5, init=True)
+    ra.ring_attn_step(tq, tk[:, :, h:].contiguous(), tv[:, :, h:].contiguous(), *halves, scale=D ** -0.5)
+    outs = []
+    for st in (whole, halves):
+        o = torch.empty_like(tq)
+        lse = torch.empty((1, 1, Hq, n), dtype=torch.float32, device="cuda")
+        ra.ring_attn_finalize(*st, o, lse)
+        outs.append((out_to_f64(o), lse.cpu().numpy()))
+    assert max_err(outs[0][0], outs[1][0]) <= 1e-2
+    assert max_err(outs[0][1], outs[1][1]) <= 1e-5
+
+
+def test_state_snapshot_and_resume(gpu_lib):
+    """The (o_acc, m, l) state after k steps is a complete checkpoint of the ring."""
+    ra = gpu_lib
+    P, n, Hq, D = 4, 128, 2, 128
+    S = P * n
+    q, k, v = _inputs(1, S, Hq, Hq, D, 1000, "bf16")
+    qs, ks, vs = (to_device(shard(x, P, "contiguous"), "bf16") for x in (q, k, v))
+    st = _state(P, 1, Hq, n, D)
+
+    def step(s, state):
+        # all devices at once: device i holds block (i - s) mod P
+        kk = torch.stack([ks[(i - s) % P] for i in range(P)]).contiguous()
+        vv = torch.stack([vs[(i - s) % P] for i in range(P)]).contiguous()
+        ra.ring_attn_step(qs, kk, vv, *state, scale=D ** -0.5, causal=True, q_off=[i * n for i in range(P)],
+                          k_off=[((i - s) % P) * n for i in range(P)], init=(s == 0))
+
+    for s in range(2):
+        step(s, st)
+    torch.cuda.synchronize()
+    saved = [x.cpu() for x in st]
+    resumed = [x.cuda() for x in saved]
+    for s in range(2, P):
+        step(s, st)
+        step(s, resumed)
+    res = []
+    for state in (st, resumed):
+        o = torch.empty_like(qs)
+        lse = torch.empty((P, 1, Hq, n), dtype=torch.float32, device="cuda")
+        ra.ring_attn_finalize(*state, o, lse)
+        res.append((out_to_f64(o), lse.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    ref_o, ref_lse = oracle.attention_reference(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"),
+                                                causal=True)
+    assert max_err(unshard_out(res[0][0], "contiguous"), ref_o) <= TOL_BF16_O
+    assert max_err(unshard_lse(res[0][1], "contiguous"), ref_lse) <= TOL_BF16_LSE
+
+
+def test_empty_and_fully_masked_edges(gpu_lib):
+    ra = gpu_lib
+    D, Hq = 128, 2
+    q, k, v = _inputs(1, 64, Hq, Hq, D, 1100, "bf16")
+    tq, tk, tv = to_device(q[None], "bf16"), to_device(k[None], "bf16"), to_device(v[None], "bf16")
+    # a block whose keys all lie after every query: skipped; with init the state is the empty state
+    st = _state(1, 1, Hq, 64, D)
+    st[0].fill_(7.0)
+    ra.ring_attn_step(tq, tk, tv, *st, scale=0.1, causal=True, q_off=[0], k_off=[64], init=True)
+    o = torch.empty_like(tq)
+    lse = torch.empty((1, 1, Hq, 64), dtype=torch.float32, device="cuda")
+    ra.ring_attn_finalize(*st, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(lse == float("-inf"))
+    # zero keys: nothing folded; zero queries: nothing to do
+    st2 = _state(1, 1, Hq, 64, D)
+    ra.ring_attn_step(tq, tk[:, :, :0].contiguous(), tv[:, :, :0].contiguous(), *st2, scale=0.1, init=True)
+    empty_state = (st2[0][:, :, :, :0].contiguous(), st2[1][:, :, :, :0].contiguous(), st2[2][:, :, :, :0].contiguous())
+    ra.ring_attn_step(tq[:, :, :0].contiguous(), tk, tv, *empty_state, scale=0.1)
+    torch.cuda.synchronize()
+    # queries that see only part of the block: partially masked rows, first rows see nothing
+    st3 = _state(1, 1, Hq, 64, D)
+    ra.ring_attn_step(tq, tk, tv, *st3, scale=D ** -0.5, causal=True, q_off=[0], k_off=[10], init=True)
+    ra.ring_attn_finalize(*st3, o, lse)
+    torch.cuda.synchronize()
+    qpos, kpos = np.arange(64), np.arange(64) + 10
+    ref_o, ref_lse = oracle.attention_reference(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"),
+                                                causal=True, q_pos=qpos, k_pos=kpos)
+    assert max_err(out_to_f64(o)[0], ref_o) <= TOL_BF16_O
+    assert max_err(lse.cpu().numpy()[0], ref_lse) <= TOL_BF16_LSE

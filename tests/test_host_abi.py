@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI library that need no GPU: it loads, exports every declared entry
+point, validates arguments before touching the GPU, and its ring planner matches the schedule and
+the work counts that follow from the pages (closed forms and brute force over positions)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import blockwise_ring_attention_step_amd as ra
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ring_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ring_attn_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ra.lib()
+    names = declared_functions()
+    assert set(names) == set(ra.EXPORTED_SYMBOLS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror():
+    assert ra.ring_attn_strerror(0) == "ok"
+    assert "invalid" in ra.ring_attn_strerror(-1)
+    assert "unsupported" in ra.ring_attn_strerror(-2)
+    assert "workspace" in ra.ring_attn_strerror(-4)
+    assert ra.ring_attn_strerror(12345) == "unknown status"
+
+
+# ---------------------------------------------------------------- planner
+
+@pytest.mark.parametrize("P,n", [(1, 16), (4, 8), (8, 2048), (32, 5)])
+@pytest.mark.parametrize("causal,striped", [(False, False), (True, False), (True, True)])
+def test_plan_follows_the_ring(P, n, causal, striped):
+    plan = ra.ring_attn_plan(P, 0, P, n, causal=causal, striped=striped)
+    assert plan.shape == (P * P, 5)
+    for s, i, j, slot, cls in plan:
+        assert j == (i - s) % P and slot == s % 2
+        if not causal:
+            assert cls == 1
+        elif striped:
+            # every block pair is partially visible (token-interleaved positions)
+            assert cls == (2 if n > 1 else (1 if j <= i else 0))
+        else:
+            assert cls == (2 if j == i else (1 if j < i else 0))
+    # each device sees every block exactly once
+    for i in range(P):
+        assert sorted(plan[plan[:, 1] == i][:, 2]) == list(range(P))
+
+
+def test_plan_for_one_device_share():
+    P, n = 32, 32768
+    plan = ra.ring_attn_plan(P, 31, 1, n, causal=True)
+    assert list(plan[:, 2]) == [(31 - s) % P for s in range(P)]
+    assert list(plan[:, 4]) == [2] + [1] * 31  # the diagonal block, then 31 fully visible blocks
+
+
+@pytest.mark.parametrize("P,n", [(4, 8), (8, 16), (8, 5), (32, 4)])
+def test_visible_pairs_match_brute_force_and_closed_forms(P, n):
+    S = P * n
+    for striped in (False, True):
+        pos = oracle.shard_positions(S, P, "striped" if striped else "contiguous")
+        for i in range(P):
+            row = [ra.ring_attn_visible_pairs(P, n, i, j, causal=True, striped=striped) for j in range(P)]
+            brute = [int((pos[j][None, :] <= pos[i][:, None]).sum()) for j in range(P)]
+            assert row == brute
+            if striped:
+                assert sum(row) == P * n * (n - 1) // 2 + (i + 1) * n
+            else:
+                assert sum(row) == i * n * n + n * (n + 1) // 2
+        assert ra.ring_attn_visible_pairs(P, n, 0, P - 1, causal=False, striped=striped) == n * n
+
+
+def test_causal_critical_path_ratio():
+    """Per-step barrier: sum over steps of the busiest device; contiguous/striped -> (2P-1)/P."""
+    for P, n in ((8, 4096), (32, 32768)):
+        crit = {}
+        for striped in (False, True):
+            crit[striped] = sum(max(ra.ring_attn_visible_pairs(P, n, i, (i - s) % P, causal=True, striped=striped)
+                                    for i in range(P)) for s in range(P))
+        ratio = crit[False] / crit[True]
+        assert abs(ratio - (2 * P - 1) / P) < 1e-3
+
+
+# ---------------------------------------------------------------- validation without a GPU
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+def _step(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, o=FAKE * 4, m=FAKE * 5, l=FAKE * 6, n_dev=1, B=1, Hq=2, Hkv=1, Nq=4,
+             Nk=4, D=16, dtype=0, scale=0.25, mask=0, q_off=None, q_stride=1, k_off=None, k_stride=1, flags=0)
+    a.update(kw)
+    arr = lambda x: None if x is None else (ctypes.c_int64 * len(x))(*x)
+    return ra.lib().ring_attn_step(a["q"], a["k"], a["v"], a["o"], a["m"], a["l"], a["n_dev"], a["B"], a["Hq"],
+                                   a["Hkv"], a["Nq"], a["Nk"], a["D"], a["dtype"], a["scale"], a["mask"],
+                                   arr(a["q_off"]), a["q_stride"], arr(a["k_off"]), a["k_stride"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(k=None), -1), (dict(n_dev=0), -1), (dict(n_dev=65), -1),
+    (dict(B=0), -1), (dict(Hq=3, Hkv=2), -1), (dict(Nq=-1), -1), (dict(D=0), -1), (dict(D=129), -2),
+    (dict(dtype=2), -1), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1), (dict(mask=2), -1),
+    (dict(mask=1), -1), (dict(mask=1, q_off=[0], k_off=[0], q_stride=0), -1), (dict(flags=4), -1),
+    (dict(o=FAKE), -1),            # state aliases q
+    (dict(m=FAKE * 4 + 16), -1),   # m inside o_acc
+])
+def test_step_rejects_bad_arguments(kw, code):
+    assert _step(**kw) == code
+
+
+def test_finalize_rejects_bad_arguments():
+    f = ra.lib().ring_attn_finalize
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 0, 1, 1, 4, 16, 0, None) == -1
+    assert f(None, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 1, 4, 16, 0, None) == -1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE, None, 1, 1, 1, 4, 16, 0, None) == -1   # o aliases o_acc
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 1, 4, 200, 0, None) == -2
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 1, 4, 16, 7, None) == -1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 1, 0, 16, 0, None) == 0  # empty: nothing to do
+
+
+def test_local_rejects_bad_arguments_and_small_workspace():
+    L = ra.lib()
+    ws = ra.ring_attn_local_workspace_bytes(4, 4, 1, 2, 1, 8, 16, 0)
+    blk = 8 * 16 * 4
+    rows = 4 * 2 * 8
+    assert ws == 4 * ((4 * blk + 255) // 256 * 256) + (rows * 16 * 4 + 255) // 256 * 256 + 2 * ((rows * 4 + 255) // 256 * 256)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE * 8, v=FAKE * 16, host=0, o=FAKE * 24, lse=None, P=4, dev0=0, n_local=4, B=1, Hq=2,
+                 Hkv=1, n=8, D=16, dtype=0, scale=0.25, mask=0, layout=0, ws=FAKE * 32, ws_bytes=ws)
+        a.update(kw)
+        return L.ring_attn_local(a["q"], a["k"], a["v"], a["host"], a["o"], a["lse"], a["P"], a["dev0"], a["n_local"],
+                                 a["B"], a["Hq"], a["Hkv"], a["n"], a["D"], a["dtype"], a["scale"], a["mask"],
+                                 a["layout"], a["ws"], a["ws_bytes"], None, None, None)
+
+    assert call(ws_bytes=ws - 1) == -4
+    assert call(P=0) == -1 and call(P=65, n_local=1) == -1
+    assert call(dev0=1) == -1           # dev0 + n_local > P
+    assert call(layout=3) == -1 and call(mask=5) == -1
+    assert call(o=FAKE) == -1           # output aliases q
+    assert call(ws=FAKE * 8) == -1      # workspace aliases k
+    assert call(D=256) == -2
+    assert call(q=None) == -1
+    assert call(n=0) == 0               # nothing to do
+    assert ra.ring_attn_local_workspace_bytes(4, 5, 1, 2, 1, 8, 16, 0) == 0
+
+
+def test_plan_rejects_bad_arguments():
+    L = ra.lib()
+    buf = (ctypes.c_int32 * 100)()
+    assert L.ring_attn_plan(0, 0, 1, 8, 0, 0, buf) == -1
+    assert L.ring_attn_plan(4, 2, 3, 8, 0, 0, buf) == -1
+    assert L.ring_attn_plan(4, 0, 4, 8, 0, 0, None) == -1
+    assert L.ring_attn_visible_pairs(4, 8, 2, 0, 0, 0) == -1
+    assert L.ring_attn_visible_pairs(4, 8, 1, 0, 4, 0) == -1
