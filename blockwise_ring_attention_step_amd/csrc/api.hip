@@ -99,12 +99,7 @@ int validate_shape(const Shape& s) {
 // Fill the work decomposition fields and launch the right kernel for the devices in p.
 hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream) {
   if (p.n_launch == 0 || p.Nq == 0) return hipSuccess;
-  if (dtype == RA_BF16 && p.D == 128) {
-    p.groups = p.n_launch * p.B * p.Hkv;
-    p.groups_per_xcd = (p.groups + 7) / 8;
-    p.n_qtiles = (p.Nq + 127) / 128;
-    return ra::launch_step_mfma_bf16_d128(p, stream);
-  }
+  if (dtype == RA_BF16 && p.D == 128) return ra::launch_step_mfma_bf16_d128(p, stream);
   return ra::launch_step_generic(p, dtype, stream);
 }
 

@@ -32,7 +32,7 @@ struct StepParams {
   int causal;
   float scale_log2;  // scale * log2(e)
   int64_t q_stride, k_stride;
-  // XCD-aware work decomposition (bf16 MFMA kernel): groups = n_launch * B * Hkv
+  // XCD-aware work decomposition, filled in by the MFMA kernel's launcher: groups = n_launch*B*Hkv
   int groups, groups_per_xcd, n_qtiles;
   int slot[RA_MAX_DEV];
   int64_t q_off[RA_MAX_DEV];

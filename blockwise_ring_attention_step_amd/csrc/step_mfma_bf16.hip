@@ -1,29 +1,39 @@
 // bf16 ring-attention step kernel for gfx950 (CDNA4), head dim 128, on v_mfma_f32_32x32x16_bf16.
 //
-// One workgroup (4 waves, 256 threads) folds one key/value block into the online-softmax state of
-// 128 query rows of one (device, batch, query head).  This is the per-step work of the Ultralytics
+// One workgroup (8 waves, 512 threads) folds one key/value block into the online-softmax state of
+// 256 query rows of one (device, batch, query head).  This is the per-step work of the Ultralytics
 // glossary page "Ring Attention", section "Como funciona a atenção em anel" (attend the held block,
 // accumulate exponentiated scores and weighted values), with the running-maximum rescaling of
 // "Sequence Parallelism and Ring Attention", section "Approfondimento tecnico".
 //
-// Data flow per 64-key tile:
-//   HBM --global_load_lds (16 B/lane, no VGPR staging)--> LDS K and V tiles (double-buffered)
-//   S^T[key, query] = K . Q^T          32x32x16 MFMA: A = K rows from LDS, B = Q^T held in VGPRs
+// Per 64-key tile t and per wave (32 query rows):
+//   S^T[key, query] = K_t . Q^T        32x32x16 MFMA: A = K rows from LDS, B = Q^T held in VGPRs
 //   online softmax in registers        lane j (mod 32) owns query j; its 32 keys per tile sit in its
 //                                      own registers, the other 32 in lane j^32: a row max needs
-//                                      one permlane32 swap, the row sum none (halves are summed once
-//                                      at the end)
-//   O^T[d, query] += V^T . P^T         A = V^T via ds_read_b64_tr_b16 (LDS transpose read), B = P^T
+//                                      one permlane32 swap, the row sum none (the two halves are
+//                                      added once at the end)
+//   O^T[d, query] += V_t^T . P^T       A = V^T via ds_read_b64_tr_b16 (LDS transpose read), B = P^T
 //                                      straight from the S^T accumulators converted to bf16
-// Because every lane owns one query row in both accumulators, rescaling O by exp2(m_old - m_new)
-// is a per-lane scalar multiply.  Rescaling is lazy: the reference exponent m only moves when a
-// tile's maximum exceeds it by more than 8 (so exponentials stay <= 2^8), which leaves the final
-// quotient exact and skips almost every rescale after the first tile.
+// Every lane owns one query row in both accumulators, so rescaling O is a per-lane scalar multiply.
+// Rescaling is lazy: the reference exponent m only moves when a tile's maximum exceeds it by more
+// than 8 (so exponentials stay <= 2^8); the final quotient is unchanged and almost every rescale
+// after the first tile is skipped.
+//
+// Ping-pong between two wave groups.  Waves 0-3 (group A, rows 0-127) and waves 4-7 (group B,
+// rows 128-255) share the SIMDs pairwise and run the same instruction sequence per tile,
+//     X_t = [scores of tile t, P.V of tile t-1]  (32 MFMAs)  barrier  Y_t = [softmax of tile t]  barrier
+// with B one barrier window behind A: while one group's X keeps the matrix pipe busy, the other
+// group's Y runs on the vector ALU.
+//
+// Memory: K and V tiles go HBM -> LDS directly (global_load_lds, 16 B per lane, no VGPR staging)
+// through 4-stage rings (K tiles in the first 64 KiB of LDS, V tiles in the next 64 KiB, so every
+// LDS address is a per-lane base plus an immediate); tile t+2 is requested while tile t is
+// computed, and a wave waits for its loads only down to one tile still in flight.
 //
 // LDS layout of a tile: 64 rows (keys) x 256 B, the 16-byte chunk c of row r stored at chunk
-// c ^ swz(r) with swz(r) = 4*(r%4) + (r/4)%4.  This makes both the 16-lane groups of the K reads
-// (16 consecutive rows, one chunk) and the 32-lane groups of the transpose reads (4 consecutive
-// rows x 4 chunks) hit distinct banks.
+// c ^ swz(r) with swz(r) = 4*(r%4) + (r/4)%4.  Both the 16-lane groups of the K reads (16
+// consecutive rows, one chunk) and the 32-lane groups of the transpose reads (4 consecutive rows x
+// 4 chunks) then hit distinct banks.
 #include "internal.h"
 
 namespace ra {
@@ -39,15 +49,21 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kD = 128;
-constexpr int kBr = 128;                      // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;              // query rows per workgroup
 constexpr int kBc = 64;                       // keys per tile
-constexpr int kThreads = 256;
 constexpr int kRowBytes = kD * 2;             // one key row of K or V in LDS
 constexpr int kTileBytes = kBc * kRowBytes;   // 16 KiB
-constexpr int kStageBytes = 2 * kTileBytes;   // K tile + V tile
-constexpr int kStages = 2;
+constexpr int kStages = 4;
+constexpr int kVRing = kStages * kTileBytes;  // LDS: K ring [0, 64 KiB), V ring [64 KiB, 128 KiB)
+constexpr int kPrefetch = 2;                  // tiles requested ahead of the one being computed
+constexpr int kPiecesPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB load instructions per tile per wave
 constexpr float kLazySlack = 8.0f;            // log2 units
 constexpr float kLn2 = 0.693147180559945309f;
+
+static_assert(kPiecesPerWave == 2, "wait counts below assume 2 K + 2 V loads per wave per tile");
+static_assert(kStages >= kPrefetch + 2, "a stage is reused only after both groups finished with it");
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -59,23 +75,8 @@ __device__ __forceinline__ float partner(float x) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// This wave's quarter of the K and V tiles starting at key0: 4 x 1 KiB pieces each, 16 B per lane.
-__device__ __forceinline__ void issue_tile_loads(const char* kbase, const char* vbase, int64_t row_bytes, int key0,
-                                                 int nk, LDS_AS char* stage, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int piece = wave * 4 + i;
-    const int row = piece * 4 + (lane >> 4);
-    const int lchunk = (lane & 15) ^ swz(row);
-    int key = key0 + row;
-    key = key < nk ? key : nk - 1;  // ragged tail: load a valid row, the mask drops it
-    const int64_t off = (int64_t)key * row_bytes + lchunk * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (LDS_AS void*)(stage + piece * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (LDS_AS void*)(stage + kTileBytes + piece * 1024),
-                                     16, 0, 0);
-  }
-}
+// all but this wave's most recent tile request (2 K + 2 V instructions) have landed in LDS
+__device__ __forceinline__ void wait_vmem_but_one_tile() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 // Largest key index visible to the query at local row `row` (causal), clamped to [-1, nk-1].
 __device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int row, int nk) {
@@ -86,13 +87,181 @@ __device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int
   return kk < (int64_t)(nk - 1) ? (int)kk : nk - 1;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void step_mfma_bf16_d128(const StepParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * kStageBytes];
+struct Ctx {
+  const char* kbase;   // this (device, batch, kv head)'s key rows, byte address of key 0
+  const char* vbase;
+  int64_t row_bytes;   // bytes between consecutive keys (Hkv * D * 2)
+  int nk;
+  uint32_t goff[kPiecesPerWave];  // byte offset of this lane's 16 B in each of its tile pieces
+};
+
+// This wave's pieces of K and V tile t into LDS stage `stage`: 16 B per lane straight from global
+// memory into LDS.  Always 2 K + 2 V instructions per call (the wait counts rely on it).
+__device__ __forceinline__ void issue_tile(const Ctx& cx, int t, LDS_AS char* smem, int stage, int wave) {
+  LDS_AS char* st = smem + stage * kTileBytes;
+  const int key0 = t * kBc;
+  if (key0 + kBc <= cx.nk) {
+    const int64_t tofs = (int64_t)key0 * cx.row_bytes;
+#pragma unroll
+    for (int i = 0; i < kPiecesPerWave; ++i) {
+      LDS_AS char* dst = st + (wave * kPiecesPerWave + i) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(cx.kbase + tofs + cx.goff[i]), (LDS_AS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(cx.vbase + tofs + cx.goff[i]), (LDS_AS void*)(dst + kVRing),
+                                       16, 0, 0);
+    }
+  } else {  // ragged last tile: rows past the end re-read the last key (the mask drops them)
+    const int lane = __lane_id();
+#pragma unroll
+    for (int i = 0; i < kPiecesPerWave; ++i) {
+      const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
+      const int key = min(key0 + row, cx.nk - 1);
+      const int64_t ofs = (int64_t)key * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16;
+      LDS_AS char* dst = st + (wave * kPiecesPerWave + i) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(cx.kbase + ofs), (LDS_AS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(cx.vbase + ofs), (LDS_AS void*)(dst + kVRing), 16, 0, 0);
+    }
+  }
+}
+
+struct Frags {
+  bf16x8 q[8];     // Q^T fragments (B operand of S^T = K Q^T)
+  int koff[8];     // LDS byte offset of this lane's K fragment for step kk (chunk 0 of the tile)
+  int voff[2][4];  // LDS byte offset of this lane's transpose reads [half][d tile] (k step 0, stage 0)
+};
+
+struct Softmax {
+  float M = -INFINITY;                    // reference exponent (log2 units)
+  float lpart[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial sums of 2^(x - M) over its keys
+};
+
+// S^T of the tile in stage ST.
+template <int ST>
+__device__ __forceinline__ void tile_scores(const Frags& f, LDS_AS char* smem, f32x16 (&s)[2]) {
+  const LDS_AS char* kt = smem + ST * kTileBytes;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    s[cc] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      bf16x8 kf = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + cc * 32 * kRowBytes + f.koff[kk]));
+      s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, f.q[kk], s[cc], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T for the tile in stage ST.
+template <int ST>
+__device__ __forceinline__ void tile_pv(const Frags& f, LDS_AS char* smem, const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
+  const LDS_AS char* vt = smem + ST * kTileBytes;  // voff includes the V ring base
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[0][dt]));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[1][dt]));
+      i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kb], o[dt], 0, 0, 0);
+    }
+}
+
+// Online-softmax update for tile t: mask (diagonal or ragged tiles), running maximum with lazy
+// rescale of O and the normaliser, P = 2^(x - M) summed in fp32 and rounded to bf16 for P.V.
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], int t, bool masked, int kmax_lane, int h2, float c,
+                                             Softmax& sm, f32x16 (&o)[4], bf16x8 (&pf)[4]) {
+  if (masked) {
+    const int kbase_idx = t * kBc + 4 * h2;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase_idx + 32 * cc + 8 * (r >> 2) + (r & 3);
+        if (key > kmax_lane) s[cc][r] = -INFINITY;
+      }
+  }
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  mx = fmaxf(mx, partner(mx));
+  const float mxs = mx * c;
+  if (__builtin_amdgcn_ballot_w64(mxs > sm.M + kLazySlack)) {
+    const float Mn = fmaxf(sm.M, mxs);
+    const float alpha = Mn > sm.M ? __builtin_amdgcn_exp2f(sm.M - Mn) : 1.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.lpart[i] *= alpha;
+    sm.M = Mn;
+  }
+  const float negM = sm.M == -INFINITY ? 0.f : -sm.M;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc][r], c, negM));
+      sm.lpart[r & 3] += e;
+      pf[2 * cc + (r >> 3)][r & 7] = (__bf16)e;
+    }
+}
+
+struct Loop {
+  int ntiles;      // tiles this workgroup loads
+  int ntiles_grp;  // tiles this wave's group computes (causal: group A may stop earlier)
+  int nfull;       // tiles [0, nfull) need no mask for any row of the group
+  int kmax_lane;
+  int h2;
+  float c;
+};
+
+// X_t: request tile t+2, scores of tile t (stage ST), P.V of tile t-1 (stage ST-1).
+template <int ST>
+__device__ __forceinline__ void phase_x(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem, int t,
+                                        int wave, f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
+  if (t + kPrefetch < lp.ntiles) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
+  if (t < lp.ntiles_grp) tile_scores<ST>(f, smem, s);
+  if (t >= 1 && t - 1 < lp.ntiles_grp) tile_pv<(ST + kStages - 1) % kStages>(f, smem, pf, o);
+}
+
+// Y_t: softmax of tile t.
+__device__ __forceinline__ void phase_y(const Loop& lp, int t, f32x16 (&s)[2], Softmax& sm, f32x16 (&o)[4],
+                                        bf16x8 (&pf)[4]) {
+  if (t < lp.ntiles_grp) tile_softmax(s, t, t >= lp.nfull, lp.kmax_lane, lp.h2, lp.c, sm, o, pf);
+}
+
+// End of a barrier window.  While tiles are still being requested, a wave's loads are complete down
+// to its most recent tile request, which covers every tile the next window reads; once requests
+// stop (drain), everything is waited for.
+__device__ __forceinline__ void window_end(bool drain) {
+  if (drain)
+    wait_vmem_all();
+  else
+    wait_vmem_but_one_tile();
+  __syncthreads();
+}
+
+// Both barrier windows of tile t (stage ST): X_t, then Y_t.  Every wave runs this same sequence;
+// group B runs it one window behind group A (one extra barrier before the loop, and group A one
+// extra barrier after it), so in each window one group is in X while the other is in Y.
+template <int ST>
+__device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem,
+                                             int t, int wave, f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm,
+                                             f32x16 (&o)[4]) {
+  const bool drain = t + kPrefetch >= lp.ntiles;
+  phase_x<ST>(cx, f, lp, smem, t, wave, s, pf, o);
+  window_end(drain);
+  phase_y(lp, t, s, sm, o, pf);
+  window_end(drain);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kVRing];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_b = wave >= kWaves / 2;
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
@@ -121,136 +290,95 @@ __global__ __launch_bounds__(kThreads, 2) void step_mfma_bf16_d128(const StepPar
   const int qr = qrow0 + wave * 32 + j;
   const bool qvalid = qr < Nq;
   const int qlast = min(qrow0 + kBr, Nq) - 1;
+  const int grow0 = min(qrow0 + (grp_b ? kBr / 2 : 0), qlast);  // this group's first and last rows
+  const int grow1 = min(qrow0 + (grp_b ? kBr : kBr / 2) - 1, qlast);
 
-  // key range of this workgroup and the per-lane causal limit
-  int kmax_lane = Nk - 1, kmin_wg = Nk - 1, kend_wg = Nk - 1;
+  // key ranges: the workgroup loads tiles up to its last row's limit; each group computes up to
+  // its own last row's limit; masks apply from the first tile its first row does not fully see
+  Loop lp;
+  lp.kmax_lane = Nk - 1;
+  int kmin_grp = Nk - 1, kend_wg = Nk - 1, kend_grp = Nk - 1;
   if (p.causal) {
-    kmax_lane = last_visible_key(p, dl, qvalid ? qr : qlast, Nk);
-    kmin_wg = last_visible_key(p, dl, qrow0, Nk);
+    lp.kmax_lane = last_visible_key(p, dl, qvalid ? qr : qlast, Nk);
+    kmin_grp = last_visible_key(p, dl, grow0, Nk);
+    kend_grp = last_visible_key(p, dl, grow1, Nk);
     kend_wg = last_visible_key(p, dl, qlast, Nk);
   }
-  const int ntiles = kend_wg < 0 ? 0 : kend_wg / kBc + 1;
-  const int nfull = kmin_wg < 0 ? 0 : (kmin_wg + 1) / kBc;  // tiles [0, nfull) need no mask
+  lp.ntiles = kend_wg < 0 ? 0 : kend_wg / kBc + 1;
+  lp.ntiles_grp = kend_grp < 0 ? 0 : kend_grp / kBc + 1;
+  lp.nfull = kmin_grp < 0 ? 0 : (kmin_grp + 1) / kBc;
+  lp.h2 = h2;
+  lp.c = p.scale_log2;
 
-  // ---- Q^T fragments (B operand): lane holds q[row qr][16*kk + 8*h2 .. +7]
+  // ---- Q^T fragments: lane holds q[row qr][16*kk + 8*h2 .. +7]
+  Frags f;
   const size_t q_dev = (size_t)p.B * Nq * Hq * kD;
   const unsigned short* qrow =
       (const unsigned short*)p.q + dev * q_dev + ((size_t)bb * Nq + (qvalid ? qr : 0)) * Hq * kD + h * kD + 8 * h2;
-  bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     i16x8 raw = qvalid ? *(const i16x8*)(qrow + 16 * kk) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    f.q[kk] = __builtin_bit_cast(bf16x8, raw);
   }
 
+  // ---- per-lane address tables
+  Ctx cx;
   const size_t kv_dev = (size_t)p.B * Nk * p.Hkv * kD;
   const size_t kv_off = 2 * (dev * kv_dev + (size_t)bb * Nk * p.Hkv * kD + (size_t)kvh * kD);
-  const char* kbase = (const char*)p.k + kv_off;
-  const char* vbase = (const char*)p.v + kv_off;
-  const int64_t row_bytes = (int64_t)p.Hkv * kD * 2;
-
-  // per-lane LDS offsets
-  const int kswz = swz(j);  // rows 32c + j share swz(j)
-  const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
-  // transpose-read row inside a 16-key step: 8*r' + 4*(tg>>1) + te; chunk 4*dt + 2*(tg&1) + (tq>>1)
-  int vrow_off[2], vswz[2];
+  cx.kbase = (const char*)p.k + kv_off;
+  cx.vbase = (const char*)p.v + kv_off;
+  cx.row_bytes = (int64_t)p.Hkv * kD * 2;
+  cx.nk = Nk;
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    vrow_off[rr] = 8 * rr + 4 * (tg >> 1) + te;
-    vswz[rr] = (te << 2) | ((2 * rr + (tg >> 1)) & 3);
+  for (int i = 0; i < kPiecesPerWave; ++i) {
+    const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
+    cx.goff[i] = (uint32_t)(row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16);
   }
-  const int vchunk0 = 2 * (tg & 1) + (tq >> 1);
-  const int vbyte = 8 * (tq & 1);
+  const int kswz = swz(j);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) f.koff[kk] = j * kRowBytes + (((2 * kk + h2) ^ kswz) * 16);
+  {
+    const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+    const int vchunk0 = 2 * (tg & 1) + (tq >> 1);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int vrow = 8 * rr + 4 * (tg >> 1) + te;
+      const int vswz = (te << 2) | ((2 * rr + (tg >> 1)) & 3);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        f.voff[rr][dt] = kVRing + vrow * kRowBytes + (((4 * dt + vchunk0) ^ vswz) * 16) + 8 * (tq & 1);
+    }
+  }
 
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float M = -INFINITY;  // reference exponent (log2 units)
-  float lsum = 0.f;     // this lane's partial sum of 2^(x - M) over its keys
-  const float c = p.scale_log2;
+  Softmax sm;
 
-  if (ntiles > 0) issue_tile_loads(kbase, vbase, row_bytes, 0, Nk, smem, wave, lane);
-
-  for (int t = 0; t < ntiles; ++t) {
-    LDS_AS char* st = smem + (t & 1) * kStageBytes;
+  if (lp.ntiles > 0) {
+    // prologue: the first kPrefetch tiles
+#pragma unroll
+    for (int t = 0; t < kPrefetch; ++t)
+      if (t < lp.ntiles) issue_tile(cx, t, smem, t, wave);
     wait_vmem_all();
     __syncthreads();
-    if (t + 1 < ntiles)
-      issue_tile_loads(kbase, vbase, row_bytes, (t + 1) * kBc, Nk, smem + ((t + 1) & 1) * kStageBytes, wave, lane);
-
-    // ---- S^T = K Q^T for keys [64t, 64t+64): two 32-key chunks
     f32x16 s[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      s[cc] = f32x16{};
-      const LDS_AS char* krow = st + (32 * cc + j) * kRowBytes;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int pch = (2 * kk + h2) ^ kswz;
-        bf16x8 kf = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(krow + pch * 16));
-        s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[cc], 0, 0, 0);
-      }
-    }
-
-    // ---- mask (diagonal / ragged tiles only): key index of register r of chunk cc
-    if (t >= nfull) {
-      const int kbase_idx = t * kBc + 4 * h2;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase_idx + 32 * cc + 8 * (r >> 2) + (r & 3);
-          if (key > kmax_lane) s[cc][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, partner(mx));
-    const float mxs = mx * c;
-    const bool need = mxs > M + kLazySlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float Mn = fmaxf(M, mxs);
-      const float alpha = Mn > M ? __builtin_amdgcn_exp2f(M - Mn) : 1.0f;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      lsum *= alpha;
-      M = Mn;
-    }
-    const float negM = M == -INFINITY ? 0.f : -M;
-    // P = 2^(x - M): summed in fp32 into the normaliser (this keeps the log-sum-exp exact to fp32),
-    // rounded to bf16 for the P.V product
     bf16x8 pf[4];
-    float lpart[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc][r], c, negM));
-        lpart[r & 3] += e;
-        pf[2 * cc + (r >> 3)][r & 7] = (__bf16)e;
-      }
-    lsum += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
-
-    // ---- O^T += V^T P^T
-    const LDS_AS char* vt = st + kTileBytes;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vt + (16 * kb + vrow_off[0]) * kRowBytes + (((4 * dt + vchunk0) ^ vswz[0]) * 16) + vbyte));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vt + (16 * kb + vrow_off[1]) * kRowBytes + (((4 * dt + vchunk0) ^ vswz[1]) * 16) + vbyte));
-        i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kb], o[dt], 0, 0, 0);
-      }
+    if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
+    // tiles 0 .. ntiles (the extra index drains the last P.V); tile t lives in stage t % 4
+    for (int t = 0; t <= lp.ntiles; t += kStages) {
+      tile_windows<0>(cx, f, lp, smem, t, wave, s, pf, sm, o);
+      if (t + 1 > lp.ntiles) break;
+      tile_windows<1>(cx, f, lp, smem, t + 1, wave, s, pf, sm, o);
+      if (t + 2 > lp.ntiles) break;
+      tile_windows<2>(cx, f, lp, smem, t + 2, wave, s, pf, sm, o);
+      if (t + 3 > lp.ntiles) break;
+      tile_windows<3>(cx, f, lp, smem, t + 3, wave, s, pf, sm, o);
     }
+    if (!grp_b) __builtin_amdgcn_s_barrier();  // matches group B's extra barrier
   }
+  float lsum = (sm.lpart[0] + sm.lpart[1]) + (sm.lpart[2] + sm.lpart[3]);
+  const float M = sm.M;
 
   // ---- epilogue: merge with the incoming state (or finalize)
   lsum += partner(lsum);
@@ -308,7 +436,11 @@ __global__ __launch_bounds__(kThreads, 2) void step_mfma_bf16_d128(const StepPar
 
 }  // namespace
 
-hipError_t launch_step_mfma_bf16_d128(const StepParams& p, hipStream_t stream) {
+hipError_t launch_step_mfma_bf16_d128(const StepParams& p_in, hipStream_t stream) {
+  StepParams p = p_in;
+  p.groups = p.n_launch * p.B * p.Hkv;
+  p.groups_per_xcd = (p.groups + 7) / 8;
+  p.n_qtiles = (p.Nq + kBr - 1) / kBr;
   const int gsz = p.Hq / p.Hkv;
   const long long grid = 8LL * p.groups_per_xcd * gsz * p.n_qtiles;
   if (grid <= 0) return hipSuccess;
