@@ -1,0 +1,151 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Each workload runs the whole ring through ``ring_attn_local`` (all emulated devices on the GPU, hop
+copies on a second stream) on seeded inputs of its real shape.  The float64 oracle is evaluated on
+at least 4096 seeded random (head, token) rows plus forced edge rows (token 0, the last token, the
+first and last row of every shard), and every sampled row is compared on all D outputs and its
+log-sum-exp: output max abs error <= 2e-2, log-sum-exp <= 1e-3 (bf16 inputs, fp32 accumulation).
+The striped causal run is also compared with the contiguous run of the same inputs after
+un-permuting, on every output element.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_ring_attention_step_amd as ra
+import oracle
+import synth_inputs as si
+from ring_harness import TOL_BF16_LSE, TOL_BF16_O, max_err
+
+pytestmark = pytest.mark.gpu
+
+N_SAMPLES = 4096
+
+
+def _shard_positions(w):
+    return oracle.shard_positions(w.S, w.P, w.layout)
+
+
+def _sample_rows(w, seed, q_tokens):
+    """(batch, head, index into q's token axis) rows: random ones plus forced edge rows."""
+    rng = np.random.default_rng(seed)
+    n_tok = q_tokens
+    flat = rng.choice(n_tok * w.Hq, size=min(N_SAMPLES, n_tok * w.Hq), replace=False)
+    rows = {(0, int(f % w.Hq), int(f // w.Hq)) for f in flat}
+    if w.local_shard is None:
+        edges = {0, w.S - 1}
+        pos = _shard_positions(w)
+        for i in range(w.P):
+            edges.add(int(pos[i, 0]))
+            edges.add(int(pos[i, -1]))
+    else:
+        edges = {0, 1, w.n - 1}
+    for t in edges:
+        for h in range(w.Hq):
+            rows.add((0, h, t))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _run(w, q, k, v):
+    """Shard, upload, run the ring; returns (o [n_local, B, n, Hq, D] bf16 tensor, lse tensor)."""
+    pos = _shard_positions(w)
+    perm = pos.reshape(-1)
+    B, n = w.B, w.n
+
+    def shard(x):
+        return np.ascontiguousarray(x[:, perm].reshape(B, w.P, n, x.shape[2], w.D).transpose(1, 0, 2, 3, 4))
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    if w.local_shard is None:
+        tq = up(shard(q))
+        dev0, n_local = 0, w.P
+    else:
+        tq = up(np.ascontiguousarray(q.reshape(B, 1, n, w.Hq, w.D).transpose(1, 0, 2, 3, 4)))
+        dev0, n_local = w.local_shard, 1
+    tk, tv = up(shard(k)), up(shard(v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((n_local, B, w.Hq, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(w.P, n_local, B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
+                     dtype=torch.uint8, device="cuda")
+    ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=1.0 / math.sqrt(w.D), causal=w.causal,
+                       striped=(w.layout == "striped"), copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    del tk, tv, ws
+    return o, lse
+
+
+def _gather(w, o, lse, rows):
+    """GPU outputs of the sampled rows (token-order indices) as float64 arrays."""
+    if w.local_shard is None:
+        pos = _shard_positions(w)
+        shard_of = np.empty(w.S, dtype=np.int64)
+        local_of = np.empty(w.S, dtype=np.int64)
+        shard_of[pos.reshape(-1)] = np.repeat(np.arange(w.P), w.n)
+        local_of[pos.reshape(-1)] = np.tile(np.arange(w.n), w.P)
+        i, r = shard_of[rows[:, 2]], local_of[rows[:, 2]]
+    else:
+        i, r = np.zeros(len(rows), dtype=np.int64), rows[:, 2]
+    ti, tb, tr, th = (torch.from_numpy(x).cuda() for x in (i, rows[:, 0], r, rows[:, 1]))
+    got_o = o[ti, tb, tr, th].float().cpu().numpy().astype(np.float64)
+    got_l = lse[ti, tb, th, tr].cpu().numpy().astype(np.float64)
+    return got_o, got_l
+
+
+def _check(name, seed):
+    w = si.WORKLOADS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    q, k, v = si.workload_qkv(w)
+    o, lse = _run(w, q, k, v)
+    rows = _sample_rows(w, seed, q.shape[1])
+    got_o, got_l = _gather(w, o, lse, rows)
+    del o, lse
+    torch.cuda.empty_cache()
+    print(f"[fullsize] {name}: oracle on {len(rows)} rows", flush=True)
+    q_pos = None if w.local_shard is None else w.local_shard * w.n + np.arange(w.n)
+    ref_o, ref_l = oracle.attention_rows(si.bf16_to_f32(q), si.bf16_to_f32(k), si.bf16_to_f32(v), rows,
+                                         causal=w.causal, q_pos=q_pos)
+    eo, el = max_err(got_o, ref_o), max_err(got_l, ref_l)
+    print(f"[fullsize] {name}: rows={len(rows)} max|dO|={eo:.3g} max|dLSE|={el:.3g}", flush=True)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+
+
+def test_noncausal_16k_eight_devices():
+    _check("noncausal_16k", 21)
+
+
+def test_causal_32k_contiguous():
+    _check("causal_32k", 31)
+
+
+def test_causal_64k_striped_gqa():
+    _check("causal_striped_64k", 41)
+
+
+def test_one_device_share_of_1m_ring():
+    _check("causal_1m_shard", 51)
+
+
+def test_striped_matches_contiguous_after_unpermuting():
+    """The same 64k causal GQA inputs under both shardings agree on every output element."""
+    ws_, wc = si.WORKLOADS["causal_striped_64k"], si.WORKLOADS["causal_contig_64k"]
+    q, k, v = si.workload_qkv(ws_)
+    outs = {}
+    for w in (ws_, wc):
+        o, lse = _run(w, q, k, v)
+        pos = torch.from_numpy(_shard_positions(w).reshape(-1)).cuda()
+        tok_o = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        tok_o[:, pos] = o.transpose(0, 1).reshape(w.B, w.S, w.Hq, w.D)
+        tok_l = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+        tok_l[:, :, pos] = lse.permute(1, 2, 0, 3).reshape(w.B, w.Hq, w.S)
+        outs[w.layout] = (tok_o, tok_l)
+        del o, lse
+        torch.cuda.empty_cache()
+    do = (outs["striped"][0].float() - outs["contiguous"][0].float()).abs().max().item()
+    dl = (outs["striped"][1] - outs["contiguous"][1]).abs().max().item()
+    print(f"[fullsize] striped vs contiguous 64k: max|dO|={do:.3g} max|dLSE|={dl:.3g}", flush=True)
+    assert math.isfinite(do) and math.isfinite(dl)
+    assert do <= TOL_BF16_O and dl <= TOL_BF16_LSE
