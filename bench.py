@@ -163,24 +163,25 @@ def cpu_baseline(w, seconds):
     rng = np.random.default_rng(7)
 
     def sample(nrows):
-        t = rng.choice(q.shape[1], size=nrows, replace=False)
-        h = rng.integers(0, w.Hq, size=nrows)
-        return np.stack([np.zeros(nrows, dtype=np.int64), h, t], axis=1)
+        flat = rng.choice(q.shape[1] * w.Hq, size=nrows, replace=False)
+        return np.stack([np.zeros(nrows, dtype=np.int64), flat % w.Hq, flat // w.Hq], axis=1)
 
     def visible(rows):
         if not w.causal:
             return float(len(rows) * w.S)
         return float(np.sum(rows[:, 2] + 1))  # contiguous token order: query t sees t+1 keys
 
-    rows = sample(64)
-    t0 = time.time()
-    oracle.attention_rows(qf, kf, vf, rows, causal=w.causal)
-    dt = time.time() - t0
-    nrows = int(min(q.shape[1] * w.Hq, max(64, 64 * seconds / max(dt, 1e-3))))
-    rows = sample(nrows)
-    t0 = time.time()
-    oracle.attention_rows(qf, kf, vf, rows, causal=w.causal)
-    dt = time.time() - t0
+    # grow the sample until one timed pass takes about `seconds` (the first pass also starts the
+    # BLAS thread pool); the work is bounded by the whole workload's rows
+    nrows, total = 64, q.shape[1] * w.Hq
+    while True:
+        rows = sample(nrows)
+        t0 = time.time()
+        oracle.attention_rows(qf, kf, vf, rows, causal=w.causal)
+        dt = time.time() - t0
+        if dt >= 0.5 * seconds or nrows >= total:
+            break
+        nrows = int(min(total, nrows * max(2.0, min(8.0, seconds / max(dt, 1e-3)))))
     fl = 4.0 * w.D * visible(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{nrows} random (head, token) rows of {w.name}, float64 NumPy, {dt:.1f} s"}
@@ -196,6 +197,8 @@ def main():
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -211,6 +214,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 3 x 1 GiB")
+        return
     w = si.WORKLOADS[args.workload]
     main_res = run_workload(w, args.steps, args.warmup)
     extras = []
