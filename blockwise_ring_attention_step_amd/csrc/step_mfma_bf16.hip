@@ -74,9 +74,11 @@ __device__ __forceinline__ float partner(float x) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt through the builtin, so the compiler's own wait bookkeeping sees it (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // all but this wave's most recent tile request (2 K + 2 V instructions) have landed in LDS
-__device__ __forceinline__ void wait_vmem_but_one_tile() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem_but_one_tile() { __builtin_amdgcn_s_waitcnt(0x0F74); }
 
 // Largest key index visible to the query at local row `row` (causal), clamped to [-1, nk-1].
 __device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int row, int nk) {
@@ -95,30 +97,45 @@ struct Ctx {
   uint32_t goff[kPiecesPerWave];  // byte offset of this lane's 16 B in each of its tile pieces
 };
 
-// This wave's pieces of K and V tile t into LDS stage `stage`: 16 B per lane straight from global
-// memory into LDS.  Always 2 K + 2 V instructions per call (the wait counts rely on it).
+// One 16-byte global -> LDS copy per lane: lane l's bytes at gbase + voff land at LDS address
+// lds + 16 l.  Issued from inline assembly so that the compiler does not treat later LDS reads of
+// other stages as possibly overlapping the copy in flight (it would otherwise wait for every
+// outstanding global load before such reads).  The kernel tracks completion itself: vmcnt waits
+// and a workgroup barrier separate every copy from the first read of its stage.
+__device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2" ::"s"(lds),
+      "v"(voff), "s"(gbase)
+      : "memory", "m0");
+}
+
+// This wave's pieces of K and V tile t into LDS stage `stage`.  Always 2 K + 2 V copies per call
+// (the wait counts rely on it).
 __device__ __forceinline__ void issue_tile(const Ctx& cx, int t, LDS_AS char* smem, int stage, int wave) {
-  LDS_AS char* st = smem + stage * kTileBytes;
+  const uint32_t st = (uint32_t)(uintptr_t)(smem + stage * kTileBytes);
   const int key0 = t * kBc;
+  const int64_t tofs = (int64_t)key0 * cx.row_bytes;
+  const char* kt = cx.kbase + tofs;
+  const char* vt = cx.vbase + tofs;
   if (key0 + kBc <= cx.nk) {
-    const int64_t tofs = (int64_t)key0 * cx.row_bytes;
 #pragma unroll
     for (int i = 0; i < kPiecesPerWave; ++i) {
-      LDS_AS char* dst = st + (wave * kPiecesPerWave + i) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(cx.kbase + tofs + cx.goff[i]), (LDS_AS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(cx.vbase + tofs + cx.goff[i]), (LDS_AS void*)(dst + kVRing),
-                                       16, 0, 0);
+      const uint32_t dst = st + (wave * kPiecesPerWave + i) * 1024;
+      copy_to_lds16(kt, cx.goff[i], dst);
+      copy_to_lds16(vt, cx.goff[i], dst + kVRing);
     }
   } else {  // ragged last tile: rows past the end re-read the last key (the mask drops them)
     const int lane = __lane_id();
 #pragma unroll
     for (int i = 0; i < kPiecesPerWave; ++i) {
       const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
-      const int key = min(key0 + row, cx.nk - 1);
-      const int64_t ofs = (int64_t)key * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16;
-      LDS_AS char* dst = st + (wave * kPiecesPerWave + i) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(cx.kbase + ofs), (LDS_AS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(cx.vbase + ofs), (LDS_AS void*)(dst + kVRing), 16, 0, 0);
+      const int krow = min(row, cx.nk - 1 - key0);
+      const uint32_t ofs = (uint32_t)(krow * cx.row_bytes) + ((lane & 15) ^ swz(row)) * 16;
+      const uint32_t dst = st + (wave * kPiecesPerWave + i) * 1024;
+      copy_to_lds16(kt, ofs, dst);
+      copy_to_lds16(vt, ofs, dst + kVRing);
     }
   }
 }
@@ -214,19 +231,74 @@ struct Loop {
   float c;
 };
 
-// X_t: request tile t+2, scores of tile t (stage ST), P.V of tile t-1 (stage ST-1).
-template <int ST>
-__device__ __forceinline__ void phase_x(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem, int t,
-                                        int wave, f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
-  if (t + kPrefetch < lp.ntiles) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
-  if (t < lp.ntiles_grp) tile_scores<ST>(f, smem, s);
-  if (t >= 1 && t - 1 < lp.ntiles_grp) tile_pv<(ST + kStages - 1) % kStages>(f, smem, pf, o);
+// The X phase as one stream of MFMAs: items 0..15 are the score products of tile t (K fragment
+// (cc = i & 1, kk = i >> 1) from stage ST; consecutive items alternate accumulators), items 16..31 the
+// P.V products of tile t-1 (V fragment (kb, dt) from the previous stage).  Each item's LDS operand is
+// read kAhead items before its MFMA into a small ring of registers, and scheduling barriers keep that
+// order, so LDS latency hides behind the MFMAs in flight instead of stalling every product.
+constexpr int kAhead = 3;
+constexpr int kRing = kAhead + 2;
+
+template <int ST, int I>
+__device__ __forceinline__ bf16x8 x_operand(const Frags& f, const LDS_AS char* smem) {
+  if constexpr (I < 16) {
+    const LDS_AS char* kt = smem + ST * kTileBytes;
+    return __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + (I & 1) * 32 * kRowBytes + f.koff[I >> 1]));
+  } else {
+    constexpr int kb = (I - 16) >> 2, dt = (I - 16) & 3;
+    const LDS_AS char* vt = smem + ((ST + kStages - 1) % kStages) * kTileBytes;  // voff includes the V ring base
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[0][dt]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[1][dt]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
-// Y_t: softmax of tile t.
+template <int I>
+__device__ __forceinline__ void x_product(const Frags& f, bf16x8 a, f32x16 (&s)[2], const bf16x8 (&pf)[4],
+                                          f32x16 (&o)[4]) {
+  if constexpr (I < 16)
+    s[I & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[I >> 1], s[I & 1], 0, 0, 0);
+  else
+    o[(I - 16) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[(I - 16) >> 2], o[(I - 16) & 3], 0, 0, 0);
+}
+
+template <int ST, int I0, int I1, int I>
+__device__ __forceinline__ void x_stream_step(const Frags& f, const LDS_AS char* smem, bf16x8 (&ring)[kRing],
+                                              f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
+  if constexpr (I < I1) {
+    if constexpr (I + kAhead < I1) ring[(I + kAhead - I0) % kRing] = x_operand<ST, I + kAhead>(f, smem);
+    __builtin_amdgcn_sched_barrier(0);
+    x_product<I>(f, ring[(I - I0) % kRing], s, pf, o);
+    __builtin_amdgcn_sched_barrier(0);
+    x_stream_step<ST, I0, I1, I + 1>(f, smem, ring, s, pf, o);
+  }
+}
+
+template <int ST, int I0, int I1>
+__device__ __forceinline__ void x_stream(const Frags& f, const LDS_AS char* smem, f32x16 (&s)[2],
+                                         const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
+  bf16x8 ring[kRing];
+  if constexpr (I0 == 0) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+  }
+  ring[0] = x_operand<ST, I0>(f, smem);
+  if constexpr (I0 + 1 < I1) ring[1] = x_operand<ST, I0 + 1>(f, smem);
+  if constexpr (I0 + 2 < I1) ring[2] = x_operand<ST, I0 + 2>(f, smem);
+  static_assert(kAhead == 3, "prologue reads kAhead operands");
+  x_stream_step<ST, I0, I1, I0>(f, smem, ring, s, pf, o);
+}
+
+// Y_t: softmax of tile t.  A tile past this group's last visible key (causal, the group of lower
+// rows) is not needed: its P is zero, so the next window's P.V adds nothing.
 __device__ __forceinline__ void phase_y(const Loop& lp, int t, f32x16 (&s)[2], Softmax& sm, f32x16 (&o)[4],
                                         bf16x8 (&pf)[4]) {
-  if (t < lp.ntiles_grp) tile_softmax(s, t, t >= lp.nfull, lp.kmax_lane, lp.h2, lp.c, sm, o, pf);
+  if (t < lp.ntiles_grp) {
+    tile_softmax(s, t, t >= lp.nfull, lp.kmax_lane, lp.h2, lp.c, sm, o, pf);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
+  }
 }
 
 // End of a barrier window.  While tiles are still being requested, a wave's loads are complete down
@@ -240,15 +312,19 @@ __device__ __forceinline__ void window_end(bool drain) {
   __syncthreads();
 }
 
-// Both barrier windows of tile t (stage ST): X_t, then Y_t.  Every wave runs this same sequence;
-// group B runs it one window behind group A (one extra barrier before the loop, and group A one
-// extra barrier after it), so in each window one group is in X while the other is in Y.
+// Both barrier windows of position t (0 <= t <= ntiles, tile t in stage ST): request tile t+2,
+// then X_t = scores of tile t and P.V of tile t-1, then Y_t.  Every position runs the same X: at
+// position 0 the P.V multiplies a zeroed V stage by P = 0, and at position ntiles the scores are
+// computed but never used, so the loop holds one X variant only.  Every wave runs this same
+// sequence; group B runs it one window behind group A (one extra barrier before the loop, and
+// group A one extra barrier after it), so in each window one group is in X while the other is in Y.
 template <int ST>
 __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem,
                                              int t, int wave, f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm,
                                              f32x16 (&o)[4]) {
   const bool drain = t + kPrefetch >= lp.ntiles;
-  phase_x<ST>(cx, f, lp, smem, t, wave, s, pf, o);
+  if (!drain) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
+  x_stream<ST, 0, 32>(f, smem, s, pf, o);
   window_end(drain);
   phase_y(lp, t, s, sm, o, pf);
   window_end(drain);
@@ -360,12 +436,19 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
 #pragma unroll
     for (int t = 0; t < kPrefetch; ++t)
       if (t < lp.ntiles) issue_tile(cx, t, smem, t, wave);
+    {  // V stage 3 feeds the P.V of position 0 (with P = 0): it must hold finite values
+      LDS_AS i16x8* z = (LDS_AS i16x8*)(smem + kVRing + 3 * kTileBytes);
+      z[tid] = i16x8{};
+      z[tid + kThreads] = i16x8{};
+    }
     wait_vmem_all();
     __syncthreads();
     f32x16 s[2];
     bf16x8 pf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
     if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
-    // tiles 0 .. ntiles (the extra index drains the last P.V); tile t lives in stage t % 4
+    // positions 0 .. ntiles (the extra position drains the last P.V); tile t lives in stage t % 4
     for (int t = 0; t <= lp.ntiles; t += kStages) {
       tile_windows<0>(cx, f, lp, smem, t, wave, s, pf, sm, o);
       if (t + 1 > lp.ntiles) break;
