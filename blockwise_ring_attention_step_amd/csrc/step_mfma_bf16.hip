@@ -59,7 +59,6 @@ constexpr int kStages = 4;
 constexpr int kVRing = kStages * kTileBytes;  // LDS: K ring [0, 64 KiB), V ring [64 KiB, 128 KiB)
 constexpr int kPrefetch = 2;                  // tiles requested ahead of the one being computed
 constexpr int kPiecesPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB load instructions per tile per wave
-constexpr float kLazySlack = 8.0f;            // log2 units
 constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kPiecesPerWave == 2, "wait counts below assume 2 K + 2 V loads per wave per tile");
@@ -102,13 +101,14 @@ struct Ctx {
 // other stages as possibly overlapping the copy in flight (it would otherwise wait for every
 // outstanding global load before such reads).  The kernel tracks completion itself: vmcnt waits
 // and a workgroup barrier separate every copy from the first read of its stage.
+// The LDS address goes in M0 (bound through the operand constraint, so the compiler knows the
+// register's value); one wait state separates the M0 write from the load.
 __device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2" ::"s"(lds),
-      "v"(voff), "s"(gbase)
-      : "memory", "m0");
+      "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
+      "s"(gbase), "{m0}"(lds)
+      : "memory");
 }
 
 // This wave's pieces of K and V tile t into LDS stage `stage`.  Always 2 K + 2 V copies per call
@@ -151,75 +151,71 @@ struct Softmax {
   float lpart[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial sums of 2^(x - M) over its keys
 };
 
-// S^T of the tile in stage ST.
-template <int ST>
-__device__ __forceinline__ void tile_scores(const Frags& f, LDS_AS char* smem, f32x16 (&s)[2]) {
-  const LDS_AS char* kt = smem + ST * kTileBytes;
-#pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    s[cc] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 kf = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + cc * 32 * kRowBytes + f.koff[kk]));
-      s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, f.q[kk], s[cc], 0, 0, 0);
-    }
-  }
-}
+// Online-softmax update for tile t: mask (diagonal or ragged tiles), then P = 2^(x - M) against
+// the row's current reference exponent M, summed in fp32 and rounded to bf16 for P.V.  The final
+// division by the normaliser cancels any choice of M, so M need not track the running maximum
+// exactly; it only has to keep the sums finite and be set once the row has seen a key.  The exact
+// row maximum (and a rescale of O and the normaliser) is therefore computed only when some lane's
+// tile sum exceeds 2^64, or a lane without a reference sees a visible key; otherwise the tile costs
+// no maximum at all.
+constexpr float kSumLimit = 0x1p64f;
 
-// O^T += V^T P^T for the tile in stage ST.
-template <int ST>
-__device__ __forceinline__ void tile_pv(const Frags& f, LDS_AS char* smem, const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
-  const LDS_AS char* vt = smem + ST * kTileBytes;  // voff includes the V ring base
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[0][dt]));
-      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[1][dt]));
-      i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kb], o[dt], 0, 0, 0);
-    }
-}
-
-// Online-softmax update for tile t: mask (diagonal or ragged tiles), running maximum with lazy
-// rescale of O and the normaliser, P = 2^(x - M) summed in fp32 and rounded to bf16 for P.V.
 __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], int t, bool masked, int kmax_lane, int h2, float c,
                                              Softmax& sm, f32x16 (&o)[4], bf16x8 (&pf)[4]) {
+  const int key_lo = t * kBc + 4 * h2;  // smallest key index this lane holds in the tile
   if (masked) {
-    const int kbase_idx = t * kBc + 4 * h2;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kbase_idx + 32 * cc + 8 * (r >> 2) + (r & 3);
+        const int key = key_lo + 32 * cc + 8 * (r >> 2) + (r & 3);
         if (key > kmax_lane) s[cc][r] = -INFINITY;
       }
   }
-  float mx = fmaxf(s[0][0], s[0][1]);
+  float e[2][16];
+  float ts[4];
+  {
+    const float negM = sm.M == -INFINITY ? 0.f : -sm.M;
 #pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-  mx = fmaxf(mx, partner(mx));
-  const float mxs = mx * c;
-  if (__builtin_amdgcn_ballot_w64(mxs > sm.M + kLazySlack)) {
-    const float Mn = fmaxf(sm.M, mxs);
+      for (int r = 0; r < 16; ++r) {
+        e[cc][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc][r], c, negM));
+        ts[r & 3] = (cc == 0 && r < 4) ? e[cc][r] : ts[r & 3] + e[cc][r];
+      }
+  }
+  const float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+  const bool first_keys = sm.M == -INFINITY && key_lo <= kmax_lane;
+  if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumLimit) || first_keys)) {
+    // new reference: the exact row maximum (both lanes of the row agree on it)
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, partner(mx));
+    const float Mn = fmaxf(sm.M, mx * c);
     const float alpha = Mn > sm.M ? __builtin_amdgcn_exp2f(sm.M - Mn) : 1.0f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm.lpart[i] *= alpha;
     sm.M = Mn;
+    const float negM = Mn == -INFINITY ? 0.f : -Mn;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[cc][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc][r], c, negM));
+        ts[r & 3] = (cc == 0 && r < 4) ? e[cc][r] : ts[r & 3] + e[cc][r];
+      }
   }
-  const float negM = sm.M == -INFINITY ? 0.f : -sm.M;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sm.lpart[i] += ts[i];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc][r], c, negM));
-      sm.lpart[r & 3] += e;
-      pf[2 * cc + (r >> 3)][r & 7] = (__bf16)e;
-    }
+    for (int r = 0; r < 16; ++r) pf[2 * cc + (r >> 3)][r & 7] = (__bf16)e[cc][r];
 }
 
 struct Loop {
@@ -231,25 +227,31 @@ struct Loop {
   float c;
 };
 
-// The X phase as one stream of MFMAs: items 0..15 are the score products of tile t (K fragment
-// (cc = i & 1, kk = i >> 1) from stage ST; consecutive items alternate accumulators), items 16..31 the
-// P.V products of tile t-1 (V fragment (kb, dt) from the previous stage).  Each item's LDS operand is
-// read kAhead items before its MFMA into a small ring of registers, and scheduling barriers keep that
-// order, so LDS latency hides behind the MFMAs in flight instead of stalling every product.
+// The X phase as one stream of 32 MFMAs: items 0..15 are the P.V products of tile t-1 (V fragment
+// (kb, dt) from the stage before ST; consecutive items use different accumulators), items 16..31 the
+// score products of tile t (K fragment (cc, kk) from stage ST, alternating accumulators).  Each
+// item's LDS operand is read kAhead items before its MFMA into a small ring of registers, and
+// scheduling barriers keep that order, so LDS latency hides behind the MFMAs in flight.  The first
+// kAhead operands (V rows of tile t-1, resident since the window before) are read at the end of the
+// previous window (x_preload), where the wave would otherwise wait at the barrier, so the stream
+// opens with an MFMA; the K rows of tile t are read only after this window's barrier, which is what
+// makes the other group's share of that tile visible.  The tile requests of the window (the hook)
+// go out behind the first two products.
 constexpr int kAhead = 3;
 constexpr int kRing = kAhead + 2;
 
 template <int ST, int I>
 __device__ __forceinline__ bf16x8 x_operand(const Frags& f, const LDS_AS char* smem) {
   if constexpr (I < 16) {
-    const LDS_AS char* kt = smem + ST * kTileBytes;
-    return __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + (I & 1) * 32 * kRowBytes + f.koff[I >> 1]));
-  } else {
-    constexpr int kb = (I - 16) >> 2, dt = (I - 16) & 3;
+    constexpr int kb = I >> 2, dt = I & 3;
     const LDS_AS char* vt = smem + ((ST + kStages - 1) % kStages) * kTileBytes;  // voff includes the V ring base
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[0][dt]));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[1][dt]));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    constexpr int cc = (I - 16) & 1, kk = (I - 16) >> 1;
+    const LDS_AS char* kt = smem + ST * kTileBytes;
+    return __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + cc * 32 * kRowBytes + f.koff[kk]));
   }
 }
 
@@ -257,36 +259,44 @@ template <int I>
 __device__ __forceinline__ void x_product(const Frags& f, bf16x8 a, f32x16 (&s)[2], const bf16x8 (&pf)[4],
                                           f32x16 (&o)[4]) {
   if constexpr (I < 16)
-    s[I & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[I >> 1], s[I & 1], 0, 0, 0);
+    o[I & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[I >> 2], o[I & 3], 0, 0, 0);
   else
-    o[(I - 16) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[(I - 16) >> 2], o[(I - 16) & 3], 0, 0, 0);
+    s[(I - 16) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[(I - 16) >> 1], s[(I - 16) & 1], 0, 0, 0);
 }
 
-template <int ST, int I0, int I1, int I>
+// The operands of items 0 .. kAhead-1 of the X phase on stage ST (V rows of the tile before ST).
+template <int ST>
+__device__ __forceinline__ void x_preload(const Frags& f, const LDS_AS char* smem, bf16x8 (&ring)[kRing]) {
+  static_assert(kAhead == 3, "x_preload reads kAhead operands");
+  ring[0] = x_operand<ST, 0>(f, smem);
+  ring[1] = x_operand<ST, 1>(f, smem);
+  ring[2] = x_operand<ST, 2>(f, smem);
+}
+
+template <int ST, int I, typename Hook>
 __device__ __forceinline__ void x_stream_step(const Frags& f, const LDS_AS char* smem, bf16x8 (&ring)[kRing],
-                                              f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
-  if constexpr (I < I1) {
-    if constexpr (I + kAhead < I1) ring[(I + kAhead - I0) % kRing] = x_operand<ST, I + kAhead>(f, smem);
+                                              f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4],
+                                              const Hook& hook) {
+  if constexpr (I < 32) {
+    if constexpr (I + kAhead < 32) ring[(I + kAhead) % kRing] = x_operand<ST, I + kAhead>(f, smem);
     __builtin_amdgcn_sched_barrier(0);
-    x_product<I>(f, ring[(I - I0) % kRing], s, pf, o);
+    x_product<I>(f, ring[I % kRing], s, pf, o);
     __builtin_amdgcn_sched_barrier(0);
-    x_stream_step<ST, I0, I1, I + 1>(f, smem, ring, s, pf, o);
+    if constexpr (I == 1) {
+      hook();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    x_stream_step<ST, I + 1>(f, smem, ring, s, pf, o, hook);
   }
 }
 
-template <int ST, int I0, int I1>
-__device__ __forceinline__ void x_stream(const Frags& f, const LDS_AS char* smem, f32x16 (&s)[2],
-                                         const bf16x8 (&pf)[4], f32x16 (&o)[4]) {
-  bf16x8 ring[kRing];
-  if constexpr (I0 == 0) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-  }
-  ring[0] = x_operand<ST, I0>(f, smem);
-  if constexpr (I0 + 1 < I1) ring[1] = x_operand<ST, I0 + 1>(f, smem);
-  if constexpr (I0 + 2 < I1) ring[2] = x_operand<ST, I0 + 2>(f, smem);
-  static_assert(kAhead == 3, "prologue reads kAhead operands");
-  x_stream_step<ST, I0, I1, I0>(f, smem, ring, s, pf, o);
+// X phase on stage ST with items 0 .. kAhead-1 already in the ring.
+template <int ST, typename Hook>
+__device__ __forceinline__ void x_stream(const Frags& f, const LDS_AS char* smem, bf16x8 (&ring)[kRing],
+                                         f32x16 (&s)[2], const bf16x8 (&pf)[4], f32x16 (&o)[4], const Hook& hook) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  x_stream_step<ST, 0>(f, smem, ring, s, pf, o, hook);
 }
 
 // Y_t: softmax of tile t.  A tile past this group's last visible key (causal, the group of lower
@@ -320,13 +330,16 @@ __device__ __forceinline__ void window_end(bool drain) {
 // group A one extra barrier after it), so in each window one group is in X while the other is in Y.
 template <int ST>
 __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem,
-                                             int t, int wave, f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm,
-                                             f32x16 (&o)[4]) {
+                                             int t, int wave, bf16x8 (&ring)[kRing], f32x16 (&s)[2],
+                                             bf16x8 (&pf)[4], Softmax& sm, f32x16 (&o)[4]) {
   const bool drain = t + kPrefetch >= lp.ntiles;
-  if (!drain) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
-  x_stream<ST, 0, 32>(f, smem, s, pf, o);
+  x_stream<ST>(f, smem, ring, s, pf, o, [&] {
+    if (!drain) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
+  });
   window_end(drain);
   phase_y(lp, t, s, sm, o, pf);
+  // the next X phase opens with the P.V of tile t, whose V rows both groups completed a window ago
+  x_preload<(ST + 1) % kStages>(f, smem, ring);
   window_end(drain);
 }
 
@@ -447,16 +460,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     bf16x8 pf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
+    bf16x8 ring[kRing];
+    x_preload<0>(f, smem, ring);
     if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
     // positions 0 .. ntiles (the extra position drains the last P.V); tile t lives in stage t % 4
     for (int t = 0; t <= lp.ntiles; t += kStages) {
-      tile_windows<0>(cx, f, lp, smem, t, wave, s, pf, sm, o);
+      tile_windows<0>(cx, f, lp, smem, t, wave, ring, s, pf, sm, o);
       if (t + 1 > lp.ntiles) break;
-      tile_windows<1>(cx, f, lp, smem, t + 1, wave, s, pf, sm, o);
+      tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, s, pf, sm, o);
       if (t + 2 > lp.ntiles) break;
-      tile_windows<2>(cx, f, lp, smem, t + 2, wave, s, pf, sm, o);
+      tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, s, pf, sm, o);
       if (t + 3 > lp.ntiles) break;
-      tile_windows<3>(cx, f, lp, smem, t + 3, wave, s, pf, sm, o);
+      tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, s, pf, sm, o);
     }
     if (!grp_b) __builtin_amdgcn_s_barrier();  // matches group B's extra barrier
   }
