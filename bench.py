@@ -30,6 +30,7 @@ METRIC = "attention TFLOP/s on 1 MI355X (causal & non-causal) + % of bf16 MFMA p
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SOURCE = os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", "step_mfma_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
+EVENT_EVERY = 4  # timed calls between two that carry per-step kernel events
 
 
 def log(msg):
@@ -97,12 +98,15 @@ def run_workload(w, steps, warmup):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [[ra.HipEvent() for _ in range(2 * w.P)] for _ in range(steps)]
+    # per-launch kernel times come from step events on every EVENT_EVERY-th timed call (each call
+    # that carries them runs ~5% slower; sampling keeps that out of most of the timed region)
+    sampled = list(range(0, steps, EVENT_EVERY))
+    ev = {i: [ra.HipEvent() for _ in range(2 * w.P)] for i in sampled}
     start, end = ra.HipEvent(), ra.HipEvent()
     torch.cuda.synchronize()
     start.record(cs)
     for i in range(steps):
-        call(ev[i])
+        call(ev.get(i))
     end.record(cs)
     torch.cuda.synchronize()
     total_ms = start.elapsed_ms(end)
@@ -117,8 +121,8 @@ def run_workload(w, steps, warmup):
         per_launch.append(4.0 * w.D * w.Hq * w.B * pairs)
     flops = sum(per_launch)
     assert abs(flops - w.flops()) <= 1e-6 * flops, (flops, w.flops())
-    kernel_ms = [[ev[i][2 * s].elapsed_ms(ev[i][2 * s + 1]) for s in range(w.P)] for i in range(steps)]
-    launch_ms = [sum(kernel_ms[i][s] for i in range(steps)) / steps for s in range(w.P)]
+    kernel_ms = [[ev[i][2 * s].elapsed_ms(ev[i][2 * s + 1]) for s in range(w.P)] for i in sampled]
+    launch_ms = [sum(k[s] for k in kernel_ms) / len(kernel_ms) for s in range(w.P)]
     kernel_total_ms = sum(launch_ms)
     achieved = flops / (kernel_total_ms * 1e-3) / 1e12  # flop-weighted average over the step launches
     tflops = flops / (ms * 1e-3) / 1e12

@@ -184,20 +184,54 @@ def ring_attn_visible_pairs(P, n, i, j, *, causal=False, striped=False) -> int:
     return int(r)
 
 
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_hiprt = None
+
+
+def _hip_runtime():
+    """The HIP runtime already loaded in this process (torch's copy, found by its soname)."""
+    global _hiprt
+    if _hiprt is None:
+        import torch  # noqa: F401  (loads the runtime)
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hiprt = h
+    return _hiprt
+
+
 class HipEvent:
-    """A timing hipEvent_t (owned by a torch.cuda.Event) whose raw handle the library can record."""
+    """A timing hipEvent_t whose raw handle the library can record between its launches.
+
+    Created without the system-scope fence, so recording it costs no cache flush on the stream it
+    times (it orders nothing for the host; the caller synchronizes before reading it)."""
 
     def __init__(self):
-        import torch
-        self._ev = torch.cuda.Event(enable_timing=True)
-        self._ev.record(torch.cuda.current_stream())  # creates the underlying hipEvent_t
-        self.handle = self._ev.cuda_event
-        if not self.handle:
-            raise RuntimeError("could not create a HIP event")
+        h = _hip_runtime()
+        ev = ctypes.c_void_p()
+        rc = h.hipEventCreateWithFlags(ctypes.byref(ev), _HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0 or not ev.value:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.handle = ev.value
+        self._h = h
 
     def record(self, stream=None):
         import torch
-        self._ev.record(torch.cuda.current_stream() if stream is None else stream)
+        st = torch.cuda.current_stream() if stream is None else stream
+        rc = self._h.hipEventRecord(self.handle, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
-        return float(self._ev.elapsed_time(end._ev))
+        ms = ctypes.c_float()
+        rc = self._h.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self._h.hipEventDestroy(self.handle)
+            self.handle = None

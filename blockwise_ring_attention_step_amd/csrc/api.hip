@@ -97,10 +97,18 @@ int validate_shape(const Shape& s) {
 }
 
 // Fill the work decomposition fields and launch the right kernel for the devices in p.
-hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream) {
-  if (p.n_launch == 0 || p.Nq == 0) return hipSuccess;
-  if (dtype == RA_BF16 && p.D == 128) return ra::launch_step_mfma_bf16_d128(p, stream);
-  return ra::launch_step_generic(p, dtype, stream);
+// ev_start / ev_stop (may be null) are stamped by the kernel launch itself; when nothing is
+// launched they are recorded on the stream so that they are still valid.
+hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr) {
+  if (p.n_launch == 0 || p.Nq == 0) {
+    hipError_t e = hipSuccess;
+    if (ev_start) e = hipEventRecord(ev_start, stream);
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
+    return e;
+  }
+  if (dtype == RA_BF16 && p.D == 128) return ra::launch_step_mfma_bf16_d128(p, stream, ev_start, ev_stop);
+  return ra::launch_step_generic(p, dtype, stream, ev_start, ev_stop);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RA_OK : RA_ERR_HIP; }
@@ -418,9 +426,8 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
       p.k_off[x] = block_offset(layout, P, n, j);
       p.dflags[x] = (s == first_step[t] ? ra::kDevInit : 0) | (s == last_step[t] ? ra::kDevFinal : 0);
     }
-    if (step_events) RA_CHECK(hipEventRecord((hipEvent_t)step_events[2 * s], cs));
-    RA_CHECK(launch_step(p, dtype, cs));
-    if (step_events) RA_CHECK(hipEventRecord((hipEvent_t)step_events[2 * s + 1], cs));
+    RA_CHECK(launch_step(p, dtype, cs, step_events ? (hipEvent_t)step_events[2 * s] : nullptr,
+                         step_events ? (hipEvent_t)step_events[2 * s + 1] : nullptr));
     RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
   // devices that never computed (no visible block): empty output

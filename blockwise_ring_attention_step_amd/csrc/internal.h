@@ -41,8 +41,10 @@ struct StepParams {
 };
 
 // Launchers (defined in the kernel sources); return a hipError_t.
-hipError_t launch_step_mfma_bf16_d128(const StepParams& p, hipStream_t stream);
-hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream);
+// ev_start / ev_stop (may be null): timing events stamped by the launch itself (no extra packets)
+hipError_t launch_step_mfma_bf16_d128(const StepParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start,
+                               hipEvent_t ev_stop);
 hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
                            int B, int Hq, int Nq, int D, int out_dtype, hipStream_t stream);
 hipError_t launch_init_state(float* o_acc, float* m, float* l, int n_dev_total, const int* slots, int n_slots,

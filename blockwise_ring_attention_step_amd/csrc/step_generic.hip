@@ -9,6 +9,8 @@
 //
 // Layout: 16 lanes cooperate on one query row (lane `sub` owns dims sub, sub+16, ...), 16 rows per
 // 256-thread workgroup; the dot product is reduced across the 16 lanes with xor shuffles.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace ra {
@@ -168,13 +170,14 @@ __global__ __launch_bounds__(256) void init_state_kernel(float* o_acc, float* m,
 
 }  // namespace
 
-hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start,
+                               hipEvent_t ev_stop) {
   if (p.Nq == 0 || p.n_launch == 0) return hipSuccess;
   dim3 grid((p.Nq + kRowsPerBlock - 1) / kRowsPerBlock, p.Hq, p.n_launch * p.B);
   if (dtype == RA_BF16)
-    hipLaunchKernelGGL(step_generic<true>, grid, dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL(step_generic<true>, grid, dim3(256), 0, stream, ev_start, ev_stop, 0, p);
   else
-    hipLaunchKernelGGL(step_generic<false>, grid, dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL(step_generic<false>, grid, dim3(256), 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

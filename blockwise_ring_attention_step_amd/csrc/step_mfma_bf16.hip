@@ -15,13 +15,13 @@
 //   O^T[d, query] += V_t^T . P^T       A = V^T via ds_read_b64_tr_b16 (LDS transpose read), B = P^T
 //                                      straight from the S^T accumulators converted to bf16
 // Every lane owns one query row in both accumulators, so rescaling O is a per-lane scalar multiply.
-// Rescaling is lazy: the reference exponent m only moves when a tile's maximum exceeds it by more
-// than 8 (so exponentials stay <= 2^8); the final quotient is unchanged and almost every rescale
-// after the first tile is skipped.
+// The reference exponent m of a row moves only when it must (the final quotient does not depend
+// on it): a tile is exponentiated against the current m, and the exact row maximum is formed only
+// when a tile sum could overflow or a row sees its first keys.
 //
 // Ping-pong between two wave groups.  Waves 0-3 (group A, rows 0-127) and waves 4-7 (group B,
 // rows 128-255) share the SIMDs pairwise and run the same instruction sequence per tile,
-//     X_t = [scores of tile t, P.V of tile t-1]  (32 MFMAs)  barrier  Y_t = [softmax of tile t]  barrier
+//     X_t = [P.V of tile t-1, scores of tile t]  (32 MFMAs)  barrier  Y_t = [softmax of tile t]  barrier
 // with B one barrier window behind A: while one group's X keeps the matrix pipe busy, the other
 // group's Y runs on the vector ALU.
 //
@@ -34,6 +34,8 @@
 // c ^ swz(r) with swz(r) = 4*(r%4) + (r/4)%4.  Both the 16-lane groups of the K reads (16
 // consecutive rows, one chunk) and the 32-lane groups of the transpose reads (4 consecutive rows x
 // 4 chunks) then hit distinct banks.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace ra {
@@ -111,33 +113,45 @@ __device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, 
       : "memory");
 }
 
-// This wave's pieces of K and V tile t into LDS stage `stage`.  Always 2 K + 2 V copies per call
-// (the wait counts rely on it).
-__device__ __forceinline__ void issue_tile(const Ctx& cx, int t, LDS_AS char* smem, int stage, int wave) {
-  const uint32_t st = (uint32_t)(uintptr_t)(smem + stage * kTileBytes);
+// This wave's share of one K/V tile request: 2 K + 2 V copies of 1 KiB (the wait counts rely on
+// exactly four).  The addresses are prepared ahead (make_request) so that the X phase only issues
+// the copies (request_piece).
+struct TileRequest {
+  const char* kt;               // global rows of the tile's first key, K and V
+  const char* vt;
+  uint32_t dst;                 // LDS address of this wave's first K piece in the stage
+  uint32_t off[kPiecesPerWave]; // per-lane byte offsets of the pieces
+};
+
+__device__ __forceinline__ TileRequest make_request(const Ctx& cx, int t, LDS_AS char* smem, int stage, int wave) {
+  TileRequest r;
   const int key0 = t * kBc;
   const int64_t tofs = (int64_t)key0 * cx.row_bytes;
-  const char* kt = cx.kbase + tofs;
-  const char* vt = cx.vbase + tofs;
+  r.kt = cx.kbase + tofs;
+  r.vt = cx.vbase + tofs;
+  r.dst = (uint32_t)(uintptr_t)(smem + stage * kTileBytes) + wave * kPiecesPerWave * 1024;
   if (key0 + kBc <= cx.nk) {
 #pragma unroll
-    for (int i = 0; i < kPiecesPerWave; ++i) {
-      const uint32_t dst = st + (wave * kPiecesPerWave + i) * 1024;
-      copy_to_lds16(kt, cx.goff[i], dst);
-      copy_to_lds16(vt, cx.goff[i], dst + kVRing);
-    }
+    for (int i = 0; i < kPiecesPerWave; ++i) r.off[i] = cx.goff[i];
   } else {  // ragged last tile: rows past the end re-read the last key (the mask drops them)
     const int lane = __lane_id();
 #pragma unroll
     for (int i = 0; i < kPiecesPerWave; ++i) {
       const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
-      const int krow = min(row, cx.nk - 1 - key0);
-      const uint32_t ofs = (uint32_t)(krow * cx.row_bytes) + ((lane & 15) ^ swz(row)) * 16;
-      const uint32_t dst = st + (wave * kPiecesPerWave + i) * 1024;
-      copy_to_lds16(kt, ofs, dst);
-      copy_to_lds16(vt, ofs, dst + kVRing);
+      const int krow = max(0, min(row, cx.nk - 1 - key0));
+      r.off[i] = (uint32_t)(krow * cx.row_bytes) + ((lane & 15) ^ swz(row)) * 16;
     }
   }
+  return r;
+}
+
+// Copy j (0..3) of a request: piece j / 2, K for even j, V for odd j.
+__device__ __forceinline__ void request_piece(const TileRequest& r, int j) {
+  const int i = j >> 1;
+  if (j & 1)
+    copy_to_lds16(r.vt, r.off[i], r.dst + i * 1024 + kVRing);
+  else
+    copy_to_lds16(r.kt, r.off[i], r.dst + i * 1024);
 }
 
 struct Frags {
@@ -227,29 +241,31 @@ struct Loop {
   float c;
 };
 
-// The X phase as one stream of 32 MFMAs: items 0..15 are the P.V products of tile t-1 (V fragment
-// (kb, dt) from the stage before ST; consecutive items use different accumulators), items 16..31 the
-// score products of tile t (K fragment (cc, kk) from stage ST, alternating accumulators).  Each
-// item's LDS operand is read kAhead items before its MFMA into a small ring of registers, and
-// scheduling barriers keep that order, so LDS latency hides behind the MFMAs in flight.  The first
-// kAhead operands (V rows of tile t-1, resident since the window before) are read at the end of the
-// previous window (x_preload), where the wave would otherwise wait at the barrier, so the stream
-// opens with an MFMA; the K rows of tile t are read only after this window's barrier, which is what
-// makes the other group's share of that tile visible.  The tile requests of the window (the hook)
-// go out behind the first two products.
+// The X phase as one stream of 32 MFMAs: the 16 P.V products of tile t-1 (V fragment (kb, dt) from
+// the stage before ST, accumulator o[dt]) and the 16 score products of tile t (K fragment (cc, kk)
+// from stage ST, accumulator s[cc]): items 0..15 are the P.V products (consecutive items use
+// different accumulators), items 16..31 the score products.  Each item's LDS operand is read
+// kAhead items before its MFMA into a small ring of registers, and scheduling barriers keep that
+// order, so LDS latency hides behind the MFMAs in flight.  The first kAhead operands (V rows of tile
+// t-1, resident since the window before) are read at the end of the previous window (x_preload),
+// where the wave would otherwise wait at the barrier, so the stream opens with an MFMA; the K rows
+// of tile t are read only after this window's barrier, which is what makes the other group's share
+// of that tile visible.  The window's tile request (addresses prepared in the previous window) goes
+// out behind the first two products (the hook).
 constexpr int kAhead = 3;
 constexpr int kRing = kAhead + 2;
 
 template <int ST, int I>
 __device__ __forceinline__ bf16x8 x_operand(const Frags& f, const LDS_AS char* smem) {
-  if constexpr (I < 16) {
-    constexpr int kb = I >> 2, dt = I & 3;
+  constexpr int P = I;
+  if constexpr (P < 16) {
+    constexpr int kb = P >> 2, dt = P & 3;
     const LDS_AS char* vt = smem + ((ST + kStages - 1) % kStages) * kTileBytes;  // voff includes the V ring base
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[0][dt]));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + kb * 16 * kRowBytes + f.voff[1][dt]));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   } else {
-    constexpr int cc = (I - 16) & 1, kk = (I - 16) >> 1;
+    constexpr int cc = (P - 16) & 1, kk = (P - 16) >> 1;
     const LDS_AS char* kt = smem + ST * kTileBytes;
     return __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(kt + cc * 32 * kRowBytes + f.koff[kk]));
   }
@@ -258,10 +274,11 @@ __device__ __forceinline__ bf16x8 x_operand(const Frags& f, const LDS_AS char* s
 template <int I>
 __device__ __forceinline__ void x_product(const Frags& f, bf16x8 a, f32x16 (&s)[2], const bf16x8 (&pf)[4],
                                           f32x16 (&o)[4]) {
-  if constexpr (I < 16)
-    o[I & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[I >> 2], o[I & 3], 0, 0, 0);
+  constexpr int P = I;
+  if constexpr (P < 16)
+    o[P & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[P >> 2], o[P & 3], 0, 0, 0);
   else
-    s[(I - 16) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[(I - 16) >> 1], s[(I - 16) & 1], 0, 0, 0);
+    s[(P - 16) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, f.q[(P - 16) >> 1], s[(P - 16) & 1], 0, 0, 0);
 }
 
 // The operands of items 0 .. kAhead-1 of the X phase on stage ST (V rows of the tile before ST).
@@ -330,16 +347,20 @@ __device__ __forceinline__ void window_end(bool drain) {
 // group A one extra barrier after it), so in each window one group is in X while the other is in Y.
 template <int ST>
 __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem,
-                                             int t, int wave, bf16x8 (&ring)[kRing], f32x16 (&s)[2],
-                                             bf16x8 (&pf)[4], Softmax& sm, f32x16 (&o)[4]) {
+                                             int t, int wave, bf16x8 (&ring)[kRing], TileRequest& req,
+                                             f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm, f32x16 (&o)[4]) {
   const bool drain = t + kPrefetch >= lp.ntiles;
   x_stream<ST>(f, smem, ring, s, pf, o, [&] {
-    if (!drain) issue_tile(cx, t + kPrefetch, smem, (ST + kPrefetch) % kStages, wave);
+    if (!drain)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) request_piece(req, j);
   });
   window_end(drain);
   phase_y(lp, t, s, sm, o, pf);
-  // the next X phase opens with the P.V of tile t, whose V rows both groups completed a window ago
+  // the next X phase opens with the P.V of tile t, whose V rows both groups completed a window ago;
+  // its tile request (tile t+3) is prepared here too, where the wave would wait at the barrier
   x_preload<(ST + 1) % kStages>(f, smem, ring);
+  req = make_request(cx, t + 1 + kPrefetch, smem, (ST + 1 + kPrefetch) % kStages, wave);
   window_end(drain);
 }
 
@@ -448,7 +469,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     // prologue: the first kPrefetch tiles
 #pragma unroll
     for (int t = 0; t < kPrefetch; ++t)
-      if (t < lp.ntiles) issue_tile(cx, t, smem, t, wave);
+      if (t < lp.ntiles) {
+        const TileRequest r = make_request(cx, t, smem, t, wave);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) request_piece(r, j);
+      }
     {  // V stage 3 feeds the P.V of position 0 (with P = 0): it must hold finite values
       LDS_AS i16x8* z = (LDS_AS i16x8*)(smem + kVRing + 3 * kTileBytes);
       z[tid] = i16x8{};
@@ -462,16 +487,17 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
     bf16x8 ring[kRing];
     x_preload<0>(f, smem, ring);
+    TileRequest req = make_request(cx, kPrefetch, smem, kPrefetch, wave);
     if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
     // positions 0 .. ntiles (the extra position drains the last P.V); tile t lives in stage t % 4
     for (int t = 0; t <= lp.ntiles; t += kStages) {
-      tile_windows<0>(cx, f, lp, smem, t, wave, ring, s, pf, sm, o);
+      tile_windows<0>(cx, f, lp, smem, t, wave, ring, req, s, pf, sm, o);
       if (t + 1 > lp.ntiles) break;
-      tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, s, pf, sm, o);
+      tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, req, s, pf, sm, o);
       if (t + 2 > lp.ntiles) break;
-      tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, s, pf, sm, o);
+      tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, req, s, pf, sm, o);
       if (t + 3 > lp.ntiles) break;
-      tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, s, pf, sm, o);
+      tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, req, s, pf, sm, o);
     }
     if (!grp_b) __builtin_amdgcn_s_barrier();  // matches group B's extra barrier
   }
@@ -534,7 +560,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
 
 }  // namespace
 
-hipError_t launch_step_mfma_bf16_d128(const StepParams& p_in, hipStream_t stream) {
+hipError_t launch_step_mfma_bf16_d128(const StepParams& p_in, hipStream_t stream, hipEvent_t ev_start,
+                                      hipEvent_t ev_stop) {
   StepParams p = p_in;
   p.groups = p.n_launch * p.B * p.Hkv;
   p.groups_per_xcd = (p.groups + 7) / 8;
@@ -543,7 +570,7 @@ hipError_t launch_step_mfma_bf16_d128(const StepParams& p_in, hipStream_t stream
   const long long grid = 8LL * p.groups_per_xcd * gsz * p.n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(step_mfma_bf16_d128, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipExtLaunchKernelGGL(step_mfma_bf16_d128, dim3((unsigned)grid), dim3(kThreads), 0, stream, ev_start, ev_stop, 0, p);
   return hipGetLastError();
 }
 

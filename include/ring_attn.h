@@ -130,8 +130,10 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  *   compute_stream, copy_stream      hipStream_t; the hops run on copy_stream, double-buffered
  *                                    against the step kernels on compute_stream (they may be equal)
  *   step_events  (may be NULL)       host array of 2*P hipEvent_t handles created by the caller;
- *                                    events 2s and 2s+1 are recorded on compute_stream around the
- *                                    step-s kernel (for timing)
+ *                                    events 2s and 2s+1 carry the start and end time of the step-s
+ *                                    kernel, stamped by its launch on compute_stream (no extra
+ *                                    stream packets); a step with nothing to launch records both
+ *                                    on compute_stream
  * Hops: a local device whose ring predecessor is also local receives the block its predecessor
  * held (a copy from that device's staging slot); otherwise the block is copied from k_src/v_src.
  * With a device-resident source a device's own block (step 0) is read in place.  Under
