@@ -8,6 +8,7 @@
 // "Ring Attention Hoạt Động Thế Nào?", describes (the next block is already being sent during the
 // current computation).  Causal blocks that are fully masked are skipped, which is the idle time of
 // the first devices that the Ultralytics page attributes to causal masking.
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -63,6 +64,26 @@ int64_t block_offset(int layout, int P, int n, int block) {
   return layout == RA_LAYOUT_STRIPED ? (int64_t)block : (int64_t)block * n;
 }
 
+// Whether the bf16 D=128 step kernel stages every key/value row of a block it computes on in the
+// workgroups that forward it (query tile qt forwards key tiles [4 qt, 4 qt + 4), which it must load):
+// the last row of each query tile has to see up to the last of those tiles.
+bool step_forward_covers(bool causal, int64_t q_off, int64_t q_stride, int Nq, int64_t k_off, int64_t k_stride,
+                         int Nk) {
+  const int br = ra::kMfmaRowsPerWg, bc = ra::kMfmaKeysPerTile;
+  const int ktiles = (Nk + bc - 1) / bc;
+  for (int qt = 0; qt * br < Nq; ++qt) {
+    const int last_row = std::min(qt * br + br - 1, Nq - 1);
+    int64_t kend = Nk - 1;
+    if (causal) {
+      const int64_t d = q_off + (int64_t)last_row * q_stride - k_off;
+      kend = d < 0 ? -1 : std::min<int64_t>(d / k_stride, Nk - 1);
+    }
+    const int loaded = kend < 0 ? 0 : (int)(kend / bc) + 1;
+    if (loaded < std::min(qt * (br / bc) + br / bc, ktiles)) return false;
+  }
+  return true;
+}
+
 int64_t layout_stride(int layout, int P) { return layout == RA_LAYOUT_STRIPED ? (int64_t)P : 1; }
 
 int64_t count_visible(int P, int n, int mask, int layout, int i, int j) {
@@ -97,6 +118,9 @@ int validate_shape(const Shape& s) {
 }
 
 // Fill the work decomposition fields and launch the right kernel for the devices in p.
+// The bf16 D = 128 steps run on the MFMA kernel; everything else on the generic one.
+bool uses_mfma_kernel(int dtype, int D) { return dtype == RA_BF16 && D == 128; }
+
 // ev_start / ev_stop (may be null) are stamped by the kernel launch itself; when nothing is
 // launched they are recorded on the stream so that they are still valid.
 hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start = nullptr,
@@ -107,7 +131,7 @@ hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream, hipEvent_t 
     if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
     return e;
   }
-  if (dtype == RA_BF16 && p.D == 128) return ra::launch_step_mfma_bf16_d128(p, stream, ev_start, ev_stop);
+  if (uses_mfma_kernel(dtype, p.D)) return ra::launch_step_mfma_bf16_d128(p, stream, ev_start, ev_stop);
   return ra::launch_step_generic(p, dtype, stream, ev_start, ev_stop);
 }
 
@@ -344,11 +368,47 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   const char* ksrc = (const char*)k_src;
   const char* vsrc = (const char*)v_src;
 
-  // copies that bring the blocks of step s into staging slot s & 1
+  // Hop plan.  With a device-resident source and the bf16 D=128 kernel, a device that computes at
+  // step s hands its block to its local successor inside the step-s kernel (the rows it stages in
+  // LDS are stored into the successor's slot); every other block of step s+1 is copied on the copy
+  // stream.  fwd_to[s*n_local+t]: successor fed by device t's step-s kernel (-1: none);
+  // by_kernel[s*n_local+t]: device t's step-s block arrives that way.
+  const bool in_step_hop = !kv_src_is_host && uses_mfma_kernel(dtype, D);
+  std::vector<int> fwd_to((size_t)P * n_local, -1);
+  std::vector<uint8_t> by_kernel((size_t)P * n_local, 0);
+  if (in_step_hop)
+    for (int s = 0; s + 1 < P; ++s)
+      for (int t = 0; t < n_local; ++t) {
+        if (cls[(size_t)s * n_local + t] == 0) continue;
+        const int succ = t + 1 < n_local ? t + 1 : (n_local == P ? 0 : -1);
+        if (succ < 0) continue;
+        const int i = dev0 + t, j = ((i - s) % P + P) % P;
+        if (!step_forward_covers(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n))
+          continue;
+        fwd_to[(size_t)s * n_local + t] = succ;
+        by_kernel[(size_t)(s + 1) * n_local + succ] = 1;
+      }
+  // whether the blocks of step s need any copy
+  auto needs_copy = [&](int s) -> bool {
+    if (s < 0 || s >= P) return false;
+    if (kv_src_is_host) return true;
+    if (s == 0) return false;  // device mode: step 0 reads the source in place
+    for (int t = 0; t < n_local; ++t)
+      if (!by_kernel[(size_t)s * n_local + t]) return true;
+    return false;
+  };
+  // device mode, s >= 1: where device t's step-s block comes from (what its predecessor held)
+  auto hop_src = [&](int s, int t, const char* src, char* const* stage) -> const char* {
+    if (t == 0 && n_local < P) return src + (size_t)(((dev0 - s) % P + P) % P) * blk;  // remote predecessor
+    const int pred = t >= 1 ? t - 1 : n_local - 1;
+    return (s == 1 ? src + (size_t)dev0 * blk : stage[(s - 1) & 1]) + (size_t)pred * blk;
+  };
+
+  // copies that bring the blocks of step s not handed over by a kernel into staging slot s & 1
   auto enqueue_hop = [&](int s) -> hipError_t {
     const int sl = s & 1;
     hipError_t e;
-    if (kv_src_is_host || s == 0) {
+    if (kv_src_is_host) {
       // every device receives block (i - s) mod P from the source (pinned host memory here)
       for (int t = 0; t < n_local; ++t) {
         const int j = ((dev0 + t - s) % P + P) % P;
@@ -357,30 +417,25 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
       }
       return hipSuccess;
     }
-    // device i receives what device i-1 held in step s-1
-    const char* prev_k = (s == 1) ? ksrc + (size_t)dev0 * blk : stage_k[sl ^ 1];
-    const char* prev_v = (s == 1) ? vsrc + (size_t)dev0 * blk : stage_v[sl ^ 1];
-    if (n_local > 1) {
-      if ((e = hipMemcpyAsync(stage_k[sl] + blk, prev_k, (n_local - 1) * blk, hipMemcpyDeviceToDevice, xs)) !=
-          hipSuccess)
-        return e;
-      if ((e = hipMemcpyAsync(stage_v[sl] + blk, prev_v, (n_local - 1) * blk, hipMemcpyDeviceToDevice, xs)) !=
-          hipSuccess)
-        return e;
+    for (int t = 0; t < n_local;) {
+      if (by_kernel[(size_t)s * n_local + t]) {
+        ++t;
+        continue;
+      }
+      // a run of devices whose sources are contiguous too
+      const char* k0 = hop_src(s, t, ksrc, stage_k);
+      const char* v0 = hop_src(s, t, vsrc, stage_v);
+      int t2 = t + 1;
+      while (t2 < n_local && !by_kernel[(size_t)s * n_local + t2] &&
+             hop_src(s, t2, ksrc, stage_k) == k0 + (size_t)(t2 - t) * blk &&
+             hop_src(s, t2, vsrc, stage_v) == v0 + (size_t)(t2 - t) * blk)
+        ++t2;
+      const size_t bytes = (size_t)(t2 - t) * blk;
+      if ((e = hipMemcpyAsync(stage_k[sl] + t * blk, k0, bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
+      if ((e = hipMemcpyAsync(stage_v[sl] + t * blk, v0, bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
+      t = t2;
     }
-    // device dev0: its predecessor is local only when the whole ring is local
-    const char* k0;
-    const char* v0;
-    if (n_local == P) {
-      k0 = prev_k + (size_t)(n_local - 1) * blk;
-      v0 = prev_v + (size_t)(n_local - 1) * blk;
-    } else {
-      const int j = ((dev0 - s) % P + P) % P;  // block arriving from the (remote) predecessor
-      k0 = ksrc + (size_t)j * blk;
-      v0 = vsrc + (size_t)j * blk;
-    }
-    if ((e = hipMemcpyAsync(stage_k[sl], k0, blk, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
-    return hipMemcpyAsync(stage_v[sl], v0, blk, hipMemcpyDeviceToDevice, xs);
+    return hipSuccess;
   };
 
   if (kv_src_is_host) {
@@ -388,14 +443,15 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
     RA_CHECK(hipEventRecord(ev_copy[0], xs));
   }
   for (int s = 0; s < P; ++s) {
-    // hop for step s+1, into the slot that step s-1 read
-    if (s + 1 < P) {
+    // copies for step s+1, into the slot that step s-1 read; they may read blocks that kernel s-1
+    // handed over, so they wait for it
+    if (needs_copy(s + 1)) {
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
       RA_CHECK(enqueue_hop(s + 1));
       RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
     }
     const bool staged = kv_src_is_host || s > 0;
-    if (staged) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
+    if (needs_copy(s)) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
 
     StepParams p{};
     p.q = q_local;
@@ -425,10 +481,13 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
       p.q_off[x] = block_offset(layout, P, n, i);
       p.k_off[x] = block_offset(layout, P, n, j);
       p.dflags[x] = (s == first_step[t] ? ra::kDevInit : 0) | (s == last_step[t] ? ra::kDevFinal : 0);
+      const int succ = fwd_to[(size_t)s * n_local + t];
+      p.fwd_k[x] = succ >= 0 ? (void*)(stage_k[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+      p.fwd_v[x] = succ >= 0 ? (void*)(stage_v[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
     }
     RA_CHECK(launch_step(p, dtype, cs, step_events ? (hipEvent_t)step_events[2 * s] : nullptr,
                          step_events ? (hipEvent_t)step_events[2 * s + 1] : nullptr));
-    RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+    if (needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
   // devices that never computed (no visible block): empty output
   for (int t = 0; t < n_local; ++t)

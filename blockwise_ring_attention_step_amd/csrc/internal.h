@@ -15,7 +15,7 @@ enum : uint8_t {
   kDevFinal = 2,  // last block of this device: write o = o_acc / l and lse instead of the state
 };
 
-// Everything one step launch needs.  Passed by value as the kernel argument (about 1.5 KiB).
+// Everything one step launch needs.  Passed by value as the kernel argument (about 2.6 KiB).
 // Device t of the launch (0 <= t < n_launch) addresses q, k, v, state and outputs at index slot[t]
 // of their leading [n_dev] dimension.
 struct StepParams {
@@ -38,7 +38,18 @@ struct StepParams {
   int64_t q_off[RA_MAX_DEV];
   int64_t k_off[RA_MAX_DEV];
   uint8_t dflags[RA_MAX_DEV];
+  // Ring hop inside the step (bf16 D=128 kernel; null: none).  The key/value rows that launch slot t
+  // stages for its computation are also written to fwd_k[t] / fwd_v[t], a [B, Nk, Hkv, D] block (the
+  // next device's receive slot), by the workgroups of the first query head of each key/value head,
+  // each the 256 keys that line up with its query tile.
+  void* fwd_k[RA_MAX_DEV];
+  void* fwd_v[RA_MAX_DEV];
 };
+
+// Work geometry of the bf16 D=128 step kernel that the host also needs (the in-step hop): query rows
+// per workgroup and keys per tile.
+constexpr int kMfmaRowsPerWg = 256;
+constexpr int kMfmaKeysPerTile = 64;
 
 // Launchers (defined in the kernel sources); return a hipError_t.
 // ev_start / ev_stop (may be null): timing events stamped by the launch itself (no extra packets)

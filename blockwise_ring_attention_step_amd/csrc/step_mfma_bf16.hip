@@ -64,6 +64,7 @@ constexpr int kPiecesPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB load instru
 constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kPiecesPerWave == 2, "wait counts below assume 2 K + 2 V loads per wave per tile");
+static_assert(kBr == kMfmaRowsPerWg && kBc == kMfmaKeysPerTile, "host view of the work geometry");
 static_assert(kStages >= kPrefetch + 2, "a stage is reused only after both groups finished with it");
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
@@ -328,15 +329,50 @@ __device__ __forceinline__ void phase_y(const Loop& lp, int t, f32x16 (&s)[2], S
   }
 }
 
-// End of a barrier window.  While tiles are still being requested, a wave's loads are complete down
-// to its most recent tile request, which covers every tile the next window reads; once requests
-// stop (drain), everything is waited for.
-__device__ __forceinline__ void window_end(bool drain) {
+// End of an X window.  While tiles are still being requested, a wave's loads are complete down to
+// its most recent tile request: that covers tile t+1, whose K rows the next X phase reads, and every
+// older copy or store; once requests stop (drain), everything is waited for.  The barrier then makes
+// every wave's share visible.
+__device__ __forceinline__ void window_end_x(bool drain) {
   if (drain)
     wait_vmem_all();
   else
     wait_vmem_but_one_tile();
   __syncthreads();
+}
+
+// End of a Y window: nothing the next window reads is in flight (tile t+1 completed at the end of
+// X_t), so no memory wait; forwarded rows may still be in flight and are covered by the next X end.
+__device__ __forceinline__ void window_end_y() { __syncthreads(); }
+
+// The ring hop inside the step: rows of the key/value block this workgroup forwards to the next
+// device's receive slot (its query tile's 256 keys, tiles [t_lo, t_hi)).
+struct Fwd {
+  char* kdst;  // destination rows of this (batch, key/value head): key 0, K and V
+  char* vdst;
+  int t_lo, t_hi;
+};
+
+// Forward tile t (stage ST): each lane stores back exactly the 16 bytes it copied into LDS, to the
+// same offset in the destination block; rows past the end of a ragged tile are not stored.
+template <int ST>
+__device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const LDS_AS char* smem, int t,
+                                             int wave) {
+  const int lane = __lane_id();
+  const int key0 = t * kBc;
+  const int64_t tofs = (int64_t)key0 * cx.row_bytes;
+#pragma unroll
+  for (int i = 0; i < kPiecesPerWave; ++i) {
+    const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
+    const LDS_AS char* src = smem + ST * kTileBytes + (wave * kPiecesPerWave + i) * 1024 + 16 * lane;
+    const i16x8 kd = *(const LDS_AS i16x8*)src;
+    const i16x8 vd = *(const LDS_AS i16x8*)(src + kVRing);
+    if (key0 + row < cx.nk) {
+      const int64_t off = tofs + (int64_t)row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16;
+      *(i16x8*)(fw.kdst + off) = kd;
+      *(i16x8*)(fw.vdst + off) = vd;
+    }
+  }
 }
 
 // Both barrier windows of position t (0 <= t <= ntiles, tile t in stage ST): request tile t+2,
@@ -348,20 +384,23 @@ __device__ __forceinline__ void window_end(bool drain) {
 template <int ST>
 __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, const Loop& lp, LDS_AS char* smem,
                                              int t, int wave, bf16x8 (&ring)[kRing], TileRequest& req,
-                                             f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm, f32x16 (&o)[4]) {
+                                             const Fwd& fw, f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm,
+                                             f32x16 (&o)[4]) {
   const bool drain = t + kPrefetch >= lp.ntiles;
   x_stream<ST>(f, smem, ring, s, pf, o, [&] {
     if (!drain)
 #pragma unroll
       for (int j = 0; j < 4; ++j) request_piece(req, j);
   });
-  window_end(drain);
+  window_end_x(drain);
   phase_y(lp, t, s, sm, o, pf);
   // the next X phase opens with the P.V of tile t, whose V rows both groups completed a window ago;
-  // its tile request (tile t+3) is prepared here too, where the wave would wait at the barrier
+  // its tile request (tile t+3) is prepared here too, where the wave would wait at the barrier, and
+  // so is the hop of tile t (this wave's copies of it completed at the end of X_{t-1})
   x_preload<(ST + 1) % kStages>(f, smem, ring);
   req = make_request(cx, t + 1 + kPrefetch, smem, (ST + 1 + kPrefetch) % kStages, wave);
-  window_end(drain);
+  if (t >= fw.t_lo && t < fw.t_hi) forward_tile<ST>(cx, fw, smem, t, wave);
+  window_end_y();
 }
 
 __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepParams p) {
@@ -444,6 +483,16 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
     cx.goff[i] = (uint32_t)(row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16);
   }
+  Fwd fw;
+  fw.kdst = fw.vdst = nullptr;
+  fw.t_lo = fw.t_hi = 0;
+  if (p.fwd_k[dl] != nullptr && hq == 0) {
+    const size_t dst_off = 2 * ((size_t)bb * Nk * p.Hkv * kD + (size_t)kvh * kD);
+    fw.kdst = (char*)p.fwd_k[dl] + dst_off;
+    fw.vdst = (char*)p.fwd_v[dl] + dst_off;
+    fw.t_lo = qt * (kBr / kBc);
+    fw.t_hi = min(fw.t_lo + kBr / kBc, lp.ntiles);
+  }
   const int kswz = swz(j);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) f.koff[kk] = j * kRowBytes + (((2 * kk + h2) ^ kswz) * 16);
@@ -491,13 +540,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
     // positions 0 .. ntiles (the extra position drains the last P.V); tile t lives in stage t % 4
     for (int t = 0; t <= lp.ntiles; t += kStages) {
-      tile_windows<0>(cx, f, lp, smem, t, wave, ring, req, s, pf, sm, o);
+      tile_windows<0>(cx, f, lp, smem, t, wave, ring, req, fw, s, pf, sm, o);
       if (t + 1 > lp.ntiles) break;
-      tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, req, s, pf, sm, o);
+      tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, req, fw, s, pf, sm, o);
       if (t + 2 > lp.ntiles) break;
-      tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, req, s, pf, sm, o);
+      tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, req, fw, s, pf, sm, o);
       if (t + 3 > lp.ntiles) break;
-      tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, req, s, pf, sm, o);
+      tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, req, fw, s, pf, sm, o);
     }
     if (!grp_b) __builtin_amdgcn_s_barrier();  // matches group B's extra barrier
   }

@@ -68,6 +68,34 @@ def test_bf16_mfma_ring(gpu_lib, causal, layout, n):
     _check_ring(gpu_lib, 2, 4, n, 4, 2, 128, causal, layout, "bf16", 200 + n)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("n", [65, 257])
+def test_bf16_mfma_ring_query_tile_edges(gpu_lib, layout, n):
+    """Causal blocks whose last query tile ends one row into a key tile: the rows of that tile reach
+    the step kernel's forwarding workgroups only partly, so those blocks travel by copy instead."""
+    _check_ring(gpu_lib, 1, 4, n, 2, 1, 128, True, layout, "bf16", 250 + n)
+
+
+@pytest.mark.parametrize("causal,layout", [(False, "contiguous"), (True, "striped")])
+def test_bf16_partly_local_ring(gpu_lib, causal, layout):
+    """Devices 2..4 of a 6-device ring run locally: the local devices hand blocks on inside the step
+    kernels, and device 2 receives from its remote predecessor by copy."""
+    P, n, Hq, Hkv, D, dev0, n_local = 6, 160, 4, 2, 128, 2, 3
+    S = P * n
+    q, k, v = _inputs(1, S, Hq, Hkv, D, 650 + causal, "bf16")
+    pos = oracle.shard_positions(S, P, layout)
+    q_local = q[:, pos[dev0:dev0 + n_local].reshape(-1)]
+    o, lse = run_ring_local(q_local, k, v, P=P, causal=causal, layout=layout, dtype="bf16", dev0=dev0,
+                            n_local=n_local)
+    toks = pos[dev0:dev0 + n_local]  # [n_local, n] token of each local row
+    rows = np.array([[0, h, int(toks[t, r])] for t in range(n_local) for h in range(Hq) for r in range(n)])
+    ref_o, ref_lse = oracle.attention_rows(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"), rows,
+                                           causal=causal)
+    got_o = np.concatenate([o[t, 0].transpose(1, 0, 2).reshape(-1, D) for t in range(n_local)])
+    got_lse = np.concatenate([lse[t, 0].reshape(-1) for t in range(n_local)])
+    assert max_err(got_o, ref_o) <= TOL_BF16_O and max_err(got_lse, ref_lse) <= TOL_BF16_LSE
+
+
 def test_bf16_mfma_ring_gqa_striped_p8(gpu_lib):
     _check_ring(gpu_lib, 1, 8, 192, 8, 2, 128, True, "striped", "bf16", 300)
 
