@@ -251,7 +251,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "P": w.P, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "mask": "causal" if w.causal else "none", "layout": w.layout,
-                   "hops": "device-to-device copies on a second stream, double-buffered"},
+                   "hops": "inside the step kernel (LDS rows stored into the successor's slot); copies otherwise"},
         "pct_of_peak": 100 * main_res["tflops"] / PEAK_BF16_TFLOPS,
         "roofline": roof, "cpu_baseline": cpu, "extra": extras,
     }
