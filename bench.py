@@ -1,14 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the per-device ring-attention hot path on one MI355X.
 
-One benchmark step = one call of ``ring_attn_local``: the whole P-step ring (hop copies on a
-second stream, one batched step kernel per ring step, the final division fused into each device's
-last step) over one batch of seeded synthetic input already resident in HBM.
+One benchmark step = one call of ``ring_attn_local``: the whole P-step ring (one batched step kernel
+per ring step that also hands each device's block to its successor, copies on a second stream for
+the blocks it cannot, the final division fused into each device's last step) over one batch of
+seeded synthetic input already resident in HBM.
 
 The default workload is the non-causal bf16 configuration the headline metric is quoted on
 (B=1, S=16384 as 8 shards of 2048, 8 heads, D=128, all 8 devices on the one GPU).  The causal
-striped grouped-query configuration (S=65536, 32 query / 8 key-value heads) is reported under
-"extra" in the same JSON line.
+workloads are reported under "extra" in the same JSON line: the striped grouped-query one (S=65536,
+32 query / 8 key-value heads), the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
+device's share of a 32-device ring over S=1048576 (8 heads); each runs about 1 s of warm-up and 2 s
+of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
+fraction of the dense bf16 MFMA rate at that clock.
 
 FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
 runs count only the visible pairs.  Printed on stdout: one JSON line.  Progress goes to stderr.
@@ -28,6 +32,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s on 1 MI355X (causal & non-causal) + % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+CUS, BF16_FLOP_PER_CLK_PER_CU = 256, 4096  # dense bf16 MFMA rate per CU per clock
+
+
+def clock_peak(sclk_mhz):
+    """Dense bf16 MFMA peak (TFLOP/s) at the measured GFX clock."""
+    return CUS * BF16_FLOP_PER_CLK_PER_CU * sclk_mhz * 1e6 / 1e12
 KERNEL_SOURCE = os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", "step_mfma_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
 EVENT_EVERY = 4  # timed calls between two that carry per-step kernel events
@@ -54,7 +64,7 @@ def shard_np(x, P, layout):
     return np.ascontiguousarray(y)
 
 
-def run_workload(w, steps, warmup):
+def run_workload(w, steps, warmup, measure_clock=True):
     import numpy as np
     import torch
 
@@ -95,6 +105,16 @@ def run_workload(w, steps, warmup):
         ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=causal, striped=striped,
                            compute_stream=cs, copy_stream=xs, step_events=events)
 
+    if warmup is None or steps is None:
+        # time-bounded extra workload: about 1 s of warm-up and 2 s of timed calls, 3 to 50 calls each
+        call()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        call()
+        torch.cuda.synchronize()
+        one = max(time.time() - t1, 1e-4)
+        warmup = max(3, min(50, int(1.0 / one)))
+        steps = max(3, min(50, int(2.0 / one)))
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -102,15 +122,16 @@ def run_workload(w, steps, warmup):
     # that carries them runs ~5% slower; sampling keeps that out of most of the timed region)
     sampled = list(range(0, steps, EVENT_EVERY))
     ev = {i: [ra.HipEvent() for _ in range(2 * w.P)] for i in sampled}
-    start, end = ra.HipEvent(), ra.HipEvent()
+    bounds = [ra.HipEvent() for _ in range(steps + 1)]  # call boundaries: per-call median and min
     torch.cuda.synchronize()
-    start.record(cs)
+    bounds[0].record(cs)
     for i in range(steps):
         call(ev.get(i))
-    end.record(cs)
+        bounds[i + 1].record(cs)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_ms(end)
+    total_ms = bounds[0].elapsed_ms(bounds[-1])
     ms = total_ms / steps
+    per_call = sorted(bounds[i].elapsed_ms(bounds[i + 1]) for i in range(steps))
 
     # algorithmic FLOPs per ring step launch (all local devices of that step)
     per_launch = []
@@ -129,11 +150,59 @@ def run_workload(w, steps, warmup):
     log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
         f"step kernels {kernel_total_ms:.3f} ms ({achieved:.1f} TFLOP/s), per step "
         + ", ".join(f"{x:.3f}" for x in launch_ms))
-    res = dict(workload=w.name, ms=ms, tflops=tflops, flops=flops, kernel_ms=kernel_total_ms,
-               kernel_tflops=achieved, launch_ms=launch_ms, launch_flops=per_launch)
+    sclk = sample_sclk(call, torch) if measure_clock else None
+    if sclk:
+        log(f"{w.name}: GFX clock under this load {sclk:.0f} MHz")
+    res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
+               ms_min=per_call[0], tflops=tflops,
+               flops=flops, kernel_ms=kernel_total_ms, kernel_tflops=achieved, launch_ms=launch_ms,
+               launch_flops=per_launch, sclk_mhz=sclk)
     del tq, tk, tv, o, lse, ws
     torch.cuda.empty_cache()
     return res
+
+
+def sample_sclk(call, torch, seconds=1.2):
+    """Median GFX clock (MHz) reported by amdsmi while the same calls keep the GPU busy: a background
+    thread samples every 10 ms while this thread keeps enqueuing calls for `seconds` (the queue
+    stays full, so every sample is taken under the load); the first third of the samples is dropped
+    (the reading lags).  None if amdsmi is unavailable."""
+    import threading
+
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # pragma: no cover
+        log(f"amdsmi unavailable ({e!r}); no clock reading")
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+            except Exception:  # pragma: no cover
+                pass
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    try:
+        th.start()
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            call()
+        stop.set()
+        th.join()
+        torch.cuda.synchronize()
+        kept = sorted(samples[len(samples) // 3:])
+        return float(kept[len(kept) // 2]) if kept else None
+    except Exception as e:  # pragma: no cover
+        log(f"clock sampling failed ({e!r})")
+        return None
+    finally:
+        stop.set()
+        amdsmi.amdsmi_shut_down()
 
 
 def traffic_entry():
@@ -198,10 +267,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
-    ap.add_argument("--extra", default="causal_striped_64k",
+    ap.add_argument("--extra", default="causal_striped_64k,causal_32k,causal_1m_shard",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amdsmi clock reading")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -228,18 +298,24 @@ def main():
         log("copied 3 x 1 GiB")
         return
     w = si.WORKLOADS[args.workload]
-    main_res = run_workload(w, args.steps, args.warmup)
+    main_res = run_workload(w, args.steps, args.warmup, not args.no_clock)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
-        r = run_workload(si.WORKLOADS[name], max(3, args.steps // 2), args.warmup)
-        extras.append({"workload": name, "value": r["tflops"], "unit": "TFLOP/s", "ms_per_step": r["ms"],
+        r = run_workload(si.WORKLOADS[name], None, None, not args.no_clock)
+        extras.append({"workload": name, "value": r["tflops"], "unit": "TFLOP/s", "steps": r["steps"],
+                       "warmup": r["warmup"], "ms_per_step": r["ms"],
+                       "ms_per_step_median": r["ms_median"], "ms_per_step_min": r["ms_min"],
                        "pct_of_peak": 100 * r["tflops"] / PEAK_BF16_TFLOPS, "step_kernel_tflops": r["kernel_tflops"],
+                       "sclk_mhz": r["sclk_mhz"],
+                       "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"]) if r["sclk_mhz"] else None),
                        "causal": si.WORKLOADS[name].causal, "layout": si.WORKLOADS[name].layout})
 
     traffic = traffic_entry()
     roof = {"bound": "mfma", "kernel": "step_mfma_bf16_d128", "achieved": main_res["kernel_tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": main_res["kernel_tflops"] / PEAK_BF16_TFLOPS,
             "traffic": traffic,
+            "frac_at_sclk": (main_res["kernel_tflops"] / clock_peak(main_res["sclk_mhz"])
+                             if main_res["sclk_mhz"] else None),
             "flops_per_launch": main_res["launch_flops"][0], "avg_launch_ms": sum(main_res["launch_ms"]) / w.P}
     cpu = None
     if not args.no_cpu_baseline:
@@ -253,6 +329,10 @@ def main():
                    "mask": "causal" if w.causal else "none", "layout": w.layout,
                    "hops": "inside the step kernel (LDS rows stored into the successor's slot); copies otherwise"},
         "pct_of_peak": 100 * main_res["tflops"] / PEAK_BF16_TFLOPS,
+        "ms_per_step_median": main_res["ms_median"], "ms_per_step_min": main_res["ms_min"],
+        "sclk_mhz": main_res["sclk_mhz"],
+        "pct_of_peak_at_sclk": (100 * main_res["tflops"] / clock_peak(main_res["sclk_mhz"])
+                                if main_res["sclk_mhz"] else None),
         "roofline": roof, "cpu_baseline": cpu, "extra": extras,
     }
     print(json.dumps(line), flush=True)

@@ -283,12 +283,13 @@ __device__ __forceinline__ void x_product(const Frags& f, bf16x8 a, f32x16 (&s)[
 }
 
 // The operands of items 0 .. kAhead-1 of the X phase on stage ST (V rows of the tile before ST).
-template <int ST>
+template <int ST, int I = 0>
 __device__ __forceinline__ void x_preload(const Frags& f, const LDS_AS char* smem, bf16x8 (&ring)[kRing]) {
-  static_assert(kAhead == 3, "x_preload reads kAhead operands");
-  ring[0] = x_operand<ST, 0>(f, smem);
-  ring[1] = x_operand<ST, 1>(f, smem);
-  ring[2] = x_operand<ST, 2>(f, smem);
+  static_assert(kAhead <= 16, "preloaded operands must all be V rows of the previous tile");
+  if constexpr (I < kAhead) {
+    ring[I] = x_operand<ST, I>(f, smem);
+    x_preload<ST, I + 1>(f, smem, ring);
+  }
 }
 
 template <int ST, int I, typename Hook>
@@ -568,38 +569,38 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   const float an = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
   const float lf = ao * lo + an * lsum;
   float* oacc_row = p.o_acc + srow * kD;
+  // the incoming accumulator rows, all requested before any store (one memory round trip, not one
+  // per chunk); this lane's chunk c covers d = 32 (c / 4) + 8 (c % 4) + 4 h2 .. + 3
+  f32x4 old[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    old[c] = has_old ? *(const f32x4*)(oacc_row + 32 * (c >> 2) + 8 * (c & 3) + 4 * h2) : f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (dfl & kDevFinal) {
     const float inv = lf > 0.f ? 1.0f / lf : 0.f;
     unsigned short* orow =
         (unsigned short*)p.o_out + (((size_t)dev * p.B + bb) * Nq + qr) * (size_t)Hq * kD + (size_t)h * kD;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int c = 0; c < 16; ++c) {
+      const int dt = c >> 2, gq = c & 3;
+      u16x4 outv;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * dt + 8 * gq + 4 * h2;
-        f32x4 old = has_old ? *(const f32x4*)(oacc_row + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-        u16x4 outv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float val = (ao * old[i] + an * o[dt][4 * gq + i]) * inv;
-          outv[i] = __builtin_bit_cast(unsigned short, (__bf16)val);
-        }
-        *(u16x4*)(orow + d0) = outv;
+      for (int i = 0; i < 4; ++i) {
+        const float val = (ao * old[c][i] + an * o[dt][4 * gq + i]) * inv;
+        outv[i] = __builtin_bit_cast(unsigned short, (__bf16)val);
       }
+      *(u16x4*)(orow + 32 * dt + 8 * gq + 4 * h2) = outv;
+    }
     if (h2 == 0 && p.lse_out) p.lse_out[srow] = lf > 0.f ? (Mf + log2f(lf)) * kLn2 : -INFINITY;
   } else {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int c = 0; c < 16; ++c) {
+      const int dt = c >> 2, gq = c & 3;
+      f32x4 nv;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * dt + 8 * gq + 4 * h2;
-        f32x4 old = has_old ? *(const f32x4*)(oacc_row + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 nv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nv[i] = ao * old[i] + an * o[dt][4 * gq + i];
-        *(f32x4*)(oacc_row + d0) = nv;
-      }
+      for (int i = 0; i < 4; ++i) nv[i] = ao * old[c][i] + an * o[dt][4 * gq + i];
+      *(f32x4*)(oacc_row + 32 * dt + 8 * gq + 4 * h2) = nv;
+    }
     if (h2 == 0) {
       p.m[srow] = Mf;
       p.l[srow] = lf;
