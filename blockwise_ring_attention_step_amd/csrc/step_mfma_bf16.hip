@@ -30,6 +30,10 @@
 // LDS address is a per-lane base plus an immediate); tile t+2 is requested while tile t is
 // computed, and a wave waits for its loads only down to one tile still in flight.
 //
+// The ring hop inside the step (optional, per device): the workgroups of the first query head of
+// each key/value head also store the key/value rows they stage in LDS into the successor device's
+// receive slot (the same pages: the next block travels while the current one is computed).
+//
 // LDS layout of a tile: 64 rows (keys) x 256 B, the 16-byte chunk c of row r stored at chunk
 // c ^ swz(r) with swz(r) = 4*(r%4) + (r/4)%4.  Both the 16-lane groups of the K reads (16
 // consecutive rows, one chunk) and the 32-lane groups of the transpose reads (4 consecutive rows x

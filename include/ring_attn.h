@@ -127,19 +127,24 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  *   workspace                        device buffer of >= ring_attn_local_workspace_bytes(...) bytes:
  *                                    two staging slots of K and V for the local devices, and the
  *                                    fp32 running state
- *   compute_stream, copy_stream      hipStream_t; the hops run on copy_stream, double-buffered
- *                                    against the step kernels on compute_stream (they may be equal)
+ *   compute_stream, copy_stream      hipStream_t; the step kernels run on compute_stream, the hops
+ *                                    that are copies on copy_stream, double-buffered against them
+ *                                    (the two may be equal)
  *   step_events  (may be NULL)       host array of 2*P hipEvent_t handles created by the caller;
  *                                    events 2s and 2s+1 carry the start and end time of the step-s
  *                                    kernel, stamped by its launch on compute_stream (no extra
  *                                    stream packets); a step with nothing to launch records both
  *                                    on compute_stream
  * Hops: a local device whose ring predecessor is also local receives the block its predecessor
- * held (a copy from that device's staging slot); otherwise the block is copied from k_src/v_src.
- * With a device-resident source a device's own block (step 0) is read in place.  Under
- * RA_MASK_CAUSAL, fully masked blocks are still passed on but not computed.  The last step of
- * each device writes o and lse directly.  The call returns after enqueueing; both streams are
- * left ordered after all of its work.
+ * held; otherwise the block comes from k_src/v_src.  With a device-resident source and the bf16
+ * D = 128 kernel, a device that computes in step s hands its block to a local successor inside the
+ * step-s kernel (the rows it stages for its own computation are stored into the successor's slot;
+ * the host checks that every row of the block is staged, else it copies); every other hop is a
+ * device-to-device (or, from pinned host memory, host-to-device) copy on copy_stream.  With a
+ * device-resident source a device's own block (step 0) is read in place.  Under RA_MASK_CAUSAL,
+ * fully masked blocks are still passed on but not computed.  The last step of each device writes
+ * o and lse directly.  The call returns after enqueueing; both streams are left ordered after all
+ * of its work.
  */
 int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
                     float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
