@@ -9,7 +9,7 @@ seeded synthetic input already resident in HBM.
 The default workload is the non-causal bf16 configuration the headline metric is quoted on
 (B=1, S=16384 as 8 shards of 2048, 8 heads, D=128, all 8 devices on the one GPU).  The causal
 workloads are reported under "extra" in the same JSON line: the striped grouped-query one (S=65536,
-32 query / 8 key-value heads), the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
+32 query / 8 key-value heads), the same inputs under zigzag sharding, the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
 device's share of a 32-device ring over S=1048576 (8 heads); each runs about 1 s of warm-up and 2 s
 of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
 fraction of the dense bf16 MFMA rate at that clock.
@@ -59,6 +59,10 @@ def shard_np(x, P, layout):
     n = S // P
     if layout == "striped":
         y = x.reshape(B, n, P, H, D).transpose(2, 0, 1, 3, 4)  # token r*P + i -> shard i, row r
+    elif layout == "zigzag":
+        c = n // 2  # 2P chunks of c tokens; shard i holds chunk i, then chunk 2P-1-i
+        ch = x.reshape(B, 2 * P, c, H, D)
+        y = np.concatenate([ch[:, :P], ch[:, P:][:, ::-1]], axis=2).transpose(1, 0, 2, 3, 4)
     else:
         y = x.reshape(B, P, n, H, D).transpose(1, 0, 2, 3, 4)
     return np.ascontiguousarray(y)
@@ -99,10 +103,9 @@ def run_workload(w, steps, warmup, measure_clock=True):
     xs = torch.cuda.Stream()
     scale = 1.0 / math.sqrt(w.D)
     causal = w.causal
-    striped = w.layout == "striped"
 
     def call(events=None):
-        ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=causal, striped=striped,
+        ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=causal, layout=w.layout,
                            compute_stream=cs, copy_stream=xs, step_events=events)
 
     if warmup is None or steps is None:
@@ -138,7 +141,7 @@ def run_workload(w, steps, warmup, measure_clock=True):
     for s in range(w.P):
         pairs = 0
         for i in range(dev0, dev0 + n_local):
-            pairs += ra.ring_attn_visible_pairs(w.P, n, i, (i - s) % w.P, causal=causal, striped=striped)
+            pairs += ra.ring_attn_visible_pairs(w.P, n, i, (i - s) % w.P, causal=causal, layout=w.layout)
         per_launch.append(4.0 * w.D * w.Hq * w.B * pairs)
     flops = sum(per_launch)
     assert abs(flops - w.flops()) <= 1e-6 * flops, (flops, w.flops())
@@ -267,7 +270,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
-    ap.add_argument("--extra", default="causal_striped_64k,causal_32k,causal_1m_shard",
+    ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -11,7 +11,17 @@ _LIB_FILE = os.path.join(_PKG_DIR, "libringattn.so")
 
 RA_F32, RA_BF16 = 0, 1
 RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
-RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
+_LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED, "zigzag": RA_LAYOUT_ZIGZAG}
+
+
+def _layout_code(layout, striped):
+    """Layout name ("contiguous", "striped", "zigzag"); the older striped flag stands for "striped"."""
+    if layout is None:
+        return RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS
+    if layout not in _LAYOUTS or (striped and layout != "striped"):
+        raise ValueError(f"unknown or conflicting layout {layout!r}")
+    return _LAYOUTS[layout]
 RA_STEP_INIT = 1
 RA_MAX_DEV, RA_MAX_D = 64, 128
 
@@ -137,12 +147,13 @@ def ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype):
 
 
 def ring_attn_local(q_local, k_src, v_src, o, lse, workspace, *, P, dev0, scale, causal=False, striped=False,
-                    compute_stream=None, copy_stream=None, step_events=None):
+                    layout=None, compute_stream=None, copy_stream=None, step_events=None):
     """Run the whole P-step ring for the local devices [dev0, dev0 + n_local).
 
     q_local [n_local, B, n, Hq, D]; k_src/v_src [P, B, n, Hkv, D] (device tensors, or pinned host
     tensors); o like q_local; lse [n_local, B, Hq, n] fp32 or None; workspace: uint8 device tensor.
     step_events: optional list of 2*P HipEvent objects recorded around each step kernel.
+    layout: "contiguous" (default), "striped" (same as striped=True) or "zigzag".
     """
     n_local, B, n, Hq, D = q_local.shape
     Hkv = k_src.shape[3]
@@ -161,24 +172,24 @@ def ring_attn_local(q_local, k_src, v_src, o, lse, workspace, *, P, dev0, scale,
     rc = lib().ring_attn_local(_ptr(q_local), kp, vp, 1 if host_src else 0, _ptr(o), _ptr(lse), P, dev0, n_local, B,
                                Hq, Hkv, n, D, _dtype_code(q_local), float(scale),
                                RA_MASK_CAUSAL if causal else RA_MASK_NONE,
-                               RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS, _ptr(workspace),
+                               _layout_code(layout, striped), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), cs, xs, ev)
     _check("ring_attn_local", rc)
 
 
-def ring_attn_plan(P, dev0, n_local, n, *, causal=False, striped=False) -> np.ndarray:
+def ring_attn_plan(P, dev0, n_local, n, *, causal=False, striped=False, layout=None) -> np.ndarray:
     """Schedule table [P * n_local, 5] of (step, device, block, slot, class)."""
     out = np.zeros((P * n_local, 5), dtype=np.int32)
     rc = lib().ring_attn_plan(P, dev0, n_local, n, RA_MASK_CAUSAL if causal else RA_MASK_NONE,
-                              RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS,
+                              _layout_code(layout, striped),
                               out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
     _check("ring_attn_plan", rc)
     return out
 
 
-def ring_attn_visible_pairs(P, n, i, j, *, causal=False, striped=False) -> int:
+def ring_attn_visible_pairs(P, n, i, j, *, causal=False, striped=False, layout=None) -> int:
     r = lib().ring_attn_visible_pairs(P, n, RA_MASK_CAUSAL if causal else RA_MASK_NONE,
-                                      RA_LAYOUT_STRIPED if striped else RA_LAYOUT_CONTIGUOUS, i, j)
+                                      _layout_code(layout, striped), i, j)
     if r < 0:
         raise RingAttnError("ring_attn_visible_pairs", -1)
     return int(r)

@@ -86,20 +86,80 @@ bool step_forward_covers(bool causal, int64_t q_off, int64_t q_stride, int Nq, i
 
 int64_t layout_stride(int layout, int P) { return layout == RA_LAYOUT_STRIPED ? (int64_t)P : 1; }
 
+bool valid_layout(int layout) {
+  return layout == RA_LAYOUT_CONTIGUOUS || layout == RA_LAYOUT_STRIPED || layout == RA_LAYOUT_ZIGZAG;
+}
+
+// Global position of local row r of block b (n rows per block).  Zigzag: the sequence is cut into
+// 2P chunks of n/2 tokens and block b holds chunks b and 2P-1-b, in that order.
+int64_t token_pos(int layout, int P, int n, int b, int64_t r) {
+  if (layout == RA_LAYOUT_STRIPED) return r * P + b;
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int64_t c = n / 2;
+    return r < c ? (int64_t)b * c + r : (2 * (int64_t)P - 1 - b) * c + (r - c);
+  }
+  return (int64_t)b * n + r;
+}
+
+// Number of key rows of block j whose position is <= pos.
+int64_t keys_upto(int layout, int P, int n, int j, int64_t pos) {
+  auto clampn = [](int64_t x, int64_t hi) { return x < 0 ? 0 : (x > hi ? hi : x); };
+  if (layout == RA_LAYOUT_STRIPED) return pos < j ? 0 : clampn((pos - j) / P + 1, n);
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int64_t c = n / 2;
+    return clampn(pos - (int64_t)j * c + 1, c) + clampn(pos - (2 * (int64_t)P - 1 - j) * c + 1, c);
+  }
+  return clampn(pos - (int64_t)j * n + 1, n);
+}
+
+// Visible (query, key) pairs between query block i and key block j: sum over query rows r of the
+// keys at or before the row's position.
 int64_t count_visible(int P, int n, int mask, int layout, int i, int j) {
   if (n <= 0) return 0;
   if (mask == RA_MASK_NONE) return (int64_t)n * n;
-  const int64_t qo = block_offset(layout, P, n, i), ko = block_offset(layout, P, n, j);
-  const int64_t st = layout_stride(layout, P);
-  // number of key rows u in [0, n) with ko + u*st <= qo + r*st, summed over query rows r
   int64_t total = 0;
-  for (int r = 0; r < n; ++r) {
-    const int64_t d = qo + (int64_t)r * st - ko;
-    if (d < 0) continue;
-    const int64_t c = d / st + 1;
-    total += c < n ? c : n;
-  }
+  for (int r = 0; r < n; ++r) total += keys_upto(layout, P, n, j, token_pos(layout, P, n, i, r));
   return total;
+}
+
+// Class of the block pair (i, j) of a ring (0 / 1 / 2 as in classify), for any layout.
+int block_class(bool causal, int P, int n, int layout, int i, int j) {
+  if (n <= 0) return 0;
+  if (layout != RA_LAYOUT_ZIGZAG) {
+    const int64_t st = layout_stride(layout, P);
+    return classify(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n);
+  }
+  const int64_t v = count_visible(P, n, causal ? RA_MASK_CAUSAL : RA_MASK_NONE, layout, i, j);
+  return v == 0 ? 0 : (v == (int64_t)n * n ? 1 : 2);
+}
+
+// One launch slot of the ring driver: query rows [row0, row0 + nq) of local device t against the
+// keys [0, nk) of the block it holds, with the positions of the first query row and first key (the
+// rows and keys are consecutive positions with stride `stride`).  The contiguous and striped layouts
+// use one unit per device (the whole block, positions of the layout); zigzag uses two, one per
+// query chunk:
+//   first chunk (positions i*c + r): the keys of chunk j (the first n/2 rows of block j);
+//   second chunk (positions (2P-1-i)*c + r): for j < i only chunk j is visible (all of it), so the
+//   unit reads the first n/2 rows; for j >= i it reads the whole block [chunk j | chunk 2P-1-j] as
+//   one run of consecutive positions ending at the true positions of chunk 2P-1-j.  Chunk j's keys
+//   then carry positions below their true ones, but still below every query of the unit (their
+//   true positions are too), so exactly the visible keys stay visible.
+struct Unit {
+  int row0, nk;
+  int64_t q_off, k_off, stride;
+};
+
+Unit ring_unit(bool causal, int layout, int P, int n, int i, int j, int half) {
+  if (layout == RA_LAYOUT_ZIGZAG && !causal) return Unit{half * (n / 2), n, 0, 0, 1};
+  if (layout != RA_LAYOUT_ZIGZAG) {
+    const int64_t st = layout_stride(layout, P);
+    return Unit{0, n, block_offset(layout, P, n, i), block_offset(layout, P, n, j), st};
+  }
+  const int c = n / 2;
+  if (half == 0) return Unit{0, c, (int64_t)i * c, (int64_t)j * c, 1};
+  const int64_t qo = (2 * (int64_t)P - 1 - i) * c;
+  if (j >= i) return Unit{c, n, qo, (2 * (int64_t)P - 2 - j) * c, 1};
+  return Unit{c, c, qo, (int64_t)j * c, 1};
 }
 
 struct Shape {
@@ -155,7 +215,7 @@ const char* ring_attn_strerror(int code) {
 int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j) {
   if (P < 1 || P > RA_MAX_DEV || n < 0 || i < 0 || j < 0 || i >= P || j >= P) return -1;
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return -1;
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return -1;
+  if (!valid_layout(layout) || (layout == RA_LAYOUT_ZIGZAG && n % 2)) return -1;
   return count_visible(P, n, mask, layout, i, j);
 }
 
@@ -163,9 +223,8 @@ int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, in
   if (P < 1 || P > RA_MAX_DEV || dev0 < 0 || dev0 >= P || n_local < 1 || dev0 + n_local > P || n < 0)
     return RA_ERR_INVALID_ARG;
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_ERR_INVALID_ARG;
+  if (!valid_layout(layout) || (layout == RA_LAYOUT_ZIGZAG && n % 2)) return RA_ERR_INVALID_ARG;
   if (!out_rows) return RA_ERR_INVALID_ARG;
-  const int64_t st = layout_stride(layout, P);
   int32_t* row = out_rows;
   for (int s = 0; s < P; ++s)
     for (int i = dev0; i < dev0 + n_local; ++i) {
@@ -174,8 +233,7 @@ int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, in
       row[1] = i;
       row[2] = j;
       row[3] = s & 1;
-      row[4] = classify(mask == RA_MASK_CAUSAL, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j),
-                        st, n);
+      row[4] = block_class(mask == RA_MASK_CAUSAL, P, n, layout, i, j);
       row += 5;
     }
   return RA_OK;
@@ -223,6 +281,8 @@ int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, fl
   p.Hkv = Hkv;
   p.Nq = Nq;
   p.Nk = Nk;
+  p.NqTot = Nq;
+  p.NkTot = Nk;
   p.D = D;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = (float)(scale * kLog2e);
@@ -238,6 +298,8 @@ int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, fl
     }
     const int i = p.n_launch++;
     p.slot[i] = t;
+    p.q_row0[i] = 0;
+    p.nk[i] = Nk;
     p.q_off[i] = qo;
     p.k_off[i] = ko;
     p.dflags[i] = (flags & RA_STEP_INIT) ? ra::kDevInit : 0;
@@ -287,7 +349,7 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   int rc = validate_shape(sh);
   if (rc != RA_OK) return rc;
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED) return RA_ERR_INVALID_ARG;
+  if (!valid_layout(layout) || (layout == RA_LAYOUT_ZIGZAG && n % 2)) return RA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
   if (n == 0) return RA_OK;
   if (!q_local || !k_src || !v_src || !o || !workspace) return RA_ERR_INVALID_ARG;
@@ -322,18 +384,22 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   const bool causal = mask == RA_MASK_CAUSAL;
   const int64_t st = layout_stride(layout, P);
 
-  // per-device schedule: first and last computed step
-  std::vector<int> first_step(n_local, -1), last_step(n_local, -1);
-  std::vector<int> cls((size_t)P * n_local);
+  // per-unit schedule (a unit is a device's whole query block, or one of its two zigzag chunks):
+  // class of every (step, unit) and each unit's first and last computed step
+  const int nh = layout == RA_LAYOUT_ZIGZAG ? 2 : 1;
+  const int n_units = n_local * nh;
+  std::vector<int> first_step(n_units, -1), last_step(n_units, -1);
+  std::vector<int> cls((size_t)P * n_units);
   for (int s = 0; s < P; ++s)
-    for (int t = 0; t < n_local; ++t) {
-      const int i = dev0 + t;
+    for (int u = 0; u < n_units; ++u) {
+      const int i = dev0 + u / nh;
       const int j = ((i - s) % P + P) % P;
-      const int c = classify(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n);
-      cls[(size_t)s * n_local + t] = c;
+      const Unit un = ring_unit(causal, layout, P, n, i, j, u % nh);
+      const int c = classify(causal, un.q_off, un.stride, n / nh, un.k_off, un.stride, un.nk);
+      cls[(size_t)s * n_units + u] = c;
       if (c != 0) {
-        if (first_step[t] < 0) first_step[t] = s;
-        last_step[t] = s;
+        if (first_step[u] < 0) first_step[u] = s;
+        last_step[u] = s;
       }
     }
 
@@ -373,7 +439,7 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   // LDS are stored into the successor's slot); every other block of step s+1 is copied on the copy
   // stream.  fwd_to[s*n_local+t]: successor fed by device t's step-s kernel (-1: none);
   // by_kernel[s*n_local+t]: device t's step-s block arrives that way.
-  const bool in_step_hop = !kv_src_is_host && uses_mfma_kernel(dtype, D);
+  const bool in_step_hop = !kv_src_is_host && uses_mfma_kernel(dtype, D) && nh == 1;
   std::vector<int> fwd_to((size_t)P * n_local, -1);
   std::vector<uint8_t> by_kernel((size_t)P * n_local, 0);
   if (in_step_hop)
@@ -465,32 +531,48 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
-    p.Nq = n;
-    p.Nk = n;
+    p.Nq = n / nh;
+    p.NqTot = n;
+    p.NkTot = n;
     p.D = D;
     p.causal = causal ? 1 : 0;
     p.scale_log2 = (float)(scale * kLog2e);
-    p.q_stride = st;
-    p.k_stride = st;
-    for (int t = 0; t < n_local; ++t) {
-      if (cls[(size_t)s * n_local + t] == 0) continue;
-      const int i = dev0 + t;
-      const int j = ((i - s) % P + P) % P;
-      const int x = p.n_launch++;
-      p.slot[x] = t;
-      p.q_off[x] = block_offset(layout, P, n, i);
-      p.k_off[x] = block_offset(layout, P, n, j);
-      p.dflags[x] = (s == first_step[t] ? ra::kDevInit : 0) | (s == last_step[t] ? ra::kDevFinal : 0);
-      const int succ = fwd_to[(size_t)s * n_local + t];
-      p.fwd_k[x] = succ >= 0 ? (void*)(stage_k[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
-      p.fwd_v[x] = succ >= 0 ? (void*)(stage_v[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+    // the units of step s, RA_MAX_DEV per launch (one launch unless zigzag with more than 32 devices)
+    std::vector<int> todo;
+    for (int u = 0; u < n_units; ++u)
+      if (cls[(size_t)s * n_units + u] != 0) todo.push_back(u);
+    const size_t n_chunks = todo.empty() ? 1 : (todo.size() + RA_MAX_DEV - 1) / RA_MAX_DEV;
+    for (size_t ch = 0; ch < n_chunks; ++ch) {
+      p.n_launch = 0;
+      p.Nk = 0;
+      for (size_t a = ch * RA_MAX_DEV; a < todo.size() && a < (ch + 1) * RA_MAX_DEV; ++a) {
+        const int u = todo[a], t = u / nh;
+        const int i = dev0 + t;
+        const int j = ((i - s) % P + P) % P;
+        const Unit un = ring_unit(causal, layout, P, n, i, j, u % nh);
+        const int x = p.n_launch++;
+        p.slot[x] = t;
+        p.q_row0[x] = un.row0;
+        p.nk[x] = un.nk;
+        p.Nk = std::max(p.Nk, un.nk);
+        p.q_off[x] = un.q_off;
+        p.k_off[x] = un.k_off;
+        p.q_stride = un.stride;  // the same for every unit of a layout
+        p.k_stride = un.stride;
+        p.dflags[x] = (s == first_step[u] ? ra::kDevInit : 0) | (s == last_step[u] ? ra::kDevFinal : 0);
+        const int succ = in_step_hop ? fwd_to[(size_t)s * n_local + t] : -1;
+        p.fwd_k[x] = succ >= 0 ? (void*)(stage_k[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+        p.fwd_v[x] = succ >= 0 ? (void*)(stage_v[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+      }
+      hipEvent_t e0 = step_events && ch == 0 ? (hipEvent_t)step_events[2 * s] : nullptr;
+      hipEvent_t e1 = step_events && ch + 1 == n_chunks ? (hipEvent_t)step_events[2 * s + 1] : nullptr;
+      RA_CHECK(launch_step(p, dtype, cs, e0, e1));
     }
-    RA_CHECK(launch_step(p, dtype, cs, step_events ? (hipEvent_t)step_events[2 * s] : nullptr,
-                         step_events ? (hipEvent_t)step_events[2 * s + 1] : nullptr));
     if (needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
-  // devices that never computed (no visible block): empty output
-  for (int t = 0; t < n_local; ++t)
+  // devices that never computed (no visible block): empty output (a zigzag unit always computes:
+  // its own block holds keys at or before each of its queries)
+  for (int t = 0; t < n_local && nh == 1; ++t)
     if (first_step[t] < 0) {
       int slot_t = t;
       RA_CHECK(ra::launch_init_state(o_acc, m_st, l_st, n_local, &slot_t, 1, B, Hq, n, D, cs));

@@ -15,20 +15,24 @@ enum : uint8_t {
   kDevFinal = 2,  // last block of this device: write o = o_acc / l and lse instead of the state
 };
 
-// Everything one step launch needs.  Passed by value as the kernel argument (about 2.6 KiB).
-// Device t of the launch (0 <= t < n_launch) addresses q, k, v, state and outputs at index slot[t]
-// of their leading [n_dev] dimension.
+// Everything one step launch needs.  Passed by value as the kernel argument (about 3.1 KiB).
+// Launch slot t (0 <= t < n_launch) addresses q, k, v, state and outputs at index slot[t] of their
+// leading [n_dev] dimension.  Within it, slot t works on the query rows [q_row0[t], q_row0[t] + Nq)
+// of the NqTot rows that the q, o_acc, m, l, o_out and lse_out arrays hold per (device, batch), and
+// reads the keys [0, nk[t]) of the NkTot rows that k and v hold per (device, batch).  A slot that
+// covers whole blocks has q_row0 = 0, Nq = NqTot and nk = NkTot.
 struct StepParams {
-  const void* q;     // [n_dev, B, Nq, Hq, D]
-  const void* k;     // [n_dev, B, Nk, Hkv, D]
-  const void* v;     // [n_dev, B, Nk, Hkv, D]
-  float* o_acc;      // [n_dev, B, Hq, Nq, D]
-  float* m;          // [n_dev, B, Hq, Nq]
-  float* l;          // [n_dev, B, Hq, Nq]
-  void* o_out;       // [n_dev, B, Nq, Hq, D] (devices with kDevFinal)
-  float* lse_out;    // [n_dev, B, Hq, Nq] or null
+  const void* q;     // [n_dev, B, NqTot, Hq, D]
+  const void* k;     // [n_dev, B, NkTot, Hkv, D]
+  const void* v;     // [n_dev, B, NkTot, Hkv, D]
+  float* o_acc;      // [n_dev, B, Hq, NqTot, D]
+  float* m;          // [n_dev, B, Hq, NqTot]
+  float* l;          // [n_dev, B, Hq, NqTot]
+  void* o_out;       // [n_dev, B, NqTot, Hq, D] (slots with kDevFinal)
+  float* lse_out;    // [n_dev, B, Hq, NqTot] or null
   int n_launch;
-  int B, Hq, Hkv, Nq, Nk, D;
+  int B, Hq, Hkv, Nq, Nk, D;  // Nq: query rows per slot; Nk: the largest nk[t]
+  int NqTot, NkTot;
   int causal;
   float scale_log2;  // scale * log2(e)
   int64_t q_stride, k_stride;
@@ -37,6 +41,8 @@ struct StepParams {
   int slot[RA_MAX_DEV];
   int64_t q_off[RA_MAX_DEV];
   int64_t k_off[RA_MAX_DEV];
+  int q_row0[RA_MAX_DEV];
+  int nk[RA_MAX_DEV];
   uint8_t dflags[RA_MAX_DEV];
   // Ring hop inside the step (bf16 D=128 kernel; null: none).  The key/value rows that launch slot t
   // stages for its computation are also written to fwd_k[t] / fwd_v[t], a [B, Nk, Hkv, D] block (the

@@ -48,13 +48,14 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   const int dl = blockIdx.z / p.B;
   const int bb = blockIdx.z % p.B;
   if (qr >= p.Nq) return;  // whole 16-lane groups leave together
-  const int D = p.D, Nq = p.Nq, Nk = p.Nk, Hq = p.Hq, Hkv = p.Hkv;
+  const int D = p.D, Hq = p.Hq, Hkv = p.Hkv;
   const int dev = p.slot[dl];
+  const int Nk = p.nk[dl], NqT = p.NqTot, NkT = p.NkTot, row = p.q_row0[dl] + qr;  // array row of this query
   const int dfl = p.dflags[dl];
   const int kvh = h / (Hq / Hkv);
 
   float q[kMaxPerLane], o[kMaxPerLane];
-  const size_t qoff = (((size_t)dev * p.B + bb) * Nq + qr) * Hq * D + (size_t)h * D;
+  const size_t qoff = (((size_t)dev * p.B + bb) * NqT + row) * Hq * D + (size_t)h * D;
 #pragma unroll
   for (int e = 0; e < kMaxPerLane; ++e) {
     const int d = sub + kLanesPerRow * e;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   const float c = p.scale_log2;
   float M = -INFINITY, l = 0.f;
   const size_t kvrow = (size_t)Hkv * D;
-  const size_t kvbase = ((size_t)dev * p.B + bb) * Nk * kvrow + (size_t)kvh * D;
+  const size_t kvbase = ((size_t)dev * p.B + bb) * NkT * kvrow + (size_t)kvh * D;
   for (int u = 0; u <= kmax; ++u) {
     float part = 0.f;
 #pragma unroll
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   }
 
   // merge with the incoming state
-  const size_t srow = (((size_t)dev * p.B + bb) * Hq + h) * Nq + qr;
+  const size_t srow = (((size_t)dev * p.B + bb) * Hq + h) * NqT + row;
   const bool has_old = !(dfl & kDevInit);
   const float Mo = has_old ? p.m[srow] : -INFINITY;
   const float lo = has_old ? p.l[srow] : 0.f;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   float* oacc = p.o_acc + srow * D;
   if (dfl & kDevFinal) {
     const float inv = lf > 0.f ? 1.0f / lf : 0.f;
-    const size_t ooff = (((size_t)dev * p.B + bb) * Nq + qr) * Hq * D + (size_t)h * D;
+    const size_t ooff = (((size_t)dev * p.B + bb) * NqT + row) * Hq * D + (size_t)h * D;
 #pragma unroll
     for (int e = 0; e < kMaxPerLane; ++e) {
       const int d = sub + kLanesPerRow * e;

@@ -438,7 +438,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   const int h = kvh * gsz + hq;
   const int dev = p.slot[dl];
   const int dfl = p.dflags[dl];
-  const int Nq = p.Nq, Nk = p.Nk, Hq = p.Hq;
+  const int Nq = p.Nq, Nk = p.nk[dl], Hq = p.Hq;
+  const int NqT = p.NqTot, NkT = p.NkTot, row0 = p.q_row0[dl];  // array rows; this slot's first row
 
   const int qrow0 = qt * kBr;
   const int qr = qrow0 + wave * 32 + j;
@@ -466,9 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
 
   // ---- Q^T fragments: lane holds q[row qr][16*kk + 8*h2 .. +7]
   Frags f;
-  const size_t q_dev = (size_t)p.B * Nq * Hq * kD;
-  const unsigned short* qrow =
-      (const unsigned short*)p.q + dev * q_dev + ((size_t)bb * Nq + (qvalid ? qr : 0)) * Hq * kD + h * kD + 8 * h2;
+  const size_t q_dev = (size_t)p.B * NqT * Hq * kD;
+  const unsigned short* qrow = (const unsigned short*)p.q + dev * q_dev +
+                               ((size_t)bb * NqT + row0 + (qvalid ? qr : 0)) * Hq * kD + h * kD + 8 * h2;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     i16x8 raw = qvalid ? *(const i16x8*)(qrow + 16 * kk) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -477,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
 
   // ---- per-lane address tables
   Ctx cx;
-  const size_t kv_dev = (size_t)p.B * Nk * p.Hkv * kD;
-  const size_t kv_off = 2 * (dev * kv_dev + (size_t)bb * Nk * p.Hkv * kD + (size_t)kvh * kD);
+  const size_t kv_dev = (size_t)p.B * NkT * p.Hkv * kD;
+  const size_t kv_off = 2 * (dev * kv_dev + (size_t)bb * NkT * p.Hkv * kD + (size_t)kvh * kD);
   cx.kbase = (const char*)p.k + kv_off;
   cx.vbase = (const char*)p.v + kv_off;
   cx.row_bytes = (int64_t)p.Hkv * kD * 2;
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   fw.kdst = fw.vdst = nullptr;
   fw.t_lo = fw.t_hi = 0;
   if (p.fwd_k[dl] != nullptr && hq == 0) {
-    const size_t dst_off = 2 * ((size_t)bb * Nk * p.Hkv * kD + (size_t)kvh * kD);
+    const size_t dst_off = 2 * ((size_t)bb * NkT * p.Hkv * kD + (size_t)kvh * kD);
     fw.kdst = (char*)p.fwd_k[dl] + dst_off;
     fw.vdst = (char*)p.fwd_v[dl] + dst_off;
     fw.t_lo = qt * (kBr / kBc);
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   // ---- epilogue: merge with the incoming state (or finalize)
   lsum += partner(lsum);
   if (!qvalid) return;
-  const size_t srow = ((size_t)(dev * p.B + bb) * Hq + h) * Nq + qr;
+  const size_t srow = ((size_t)(dev * p.B + bb) * Hq + h) * NqT + row0 + qr;
   float Mo = -INFINITY, lo = 0.f;
   const bool has_old = !(dfl & kDevInit);
   if (has_old) {
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   if (dfl & kDevFinal) {
     const float inv = lf > 0.f ? 1.0f / lf : 0.f;
     unsigned short* orow =
-        (unsigned short*)p.o_out + (((size_t)dev * p.B + bb) * Nq + qr) * (size_t)Hq * kD + (size_t)h * kD;
+        (unsigned short*)p.o_out + (((size_t)dev * p.B + bb) * NqT + row0 + qr) * (size_t)Hq * kD + (size_t)h * kD;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const int dt = c >> 2, gq = c & 3;

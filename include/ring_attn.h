@@ -30,6 +30,10 @@
  *   - Token positions: local row r of device t has global position  off[t] + r * stride.  With
  *     contiguous sharding off[t] = t*n, stride = 1; with striped sharding (token p on shard p mod P)
  *     off[t] = t, stride = P.  Under RA_MASK_CAUSAL key u is visible to query t iff pos(u) <= pos(t).
+ *     The zigzag layout of ring_attn_local (shard i holds the chunks i and 2P-1-i of n/2 tokens, the
+ *     second of the balancing variants named next to striped attention on "Ukulandelana
+ *     Ukuhambisana Nokunakwa Kwendandatho" (aiunderstanding.org), section "Ikusasa Lokulandelana
+ *     Ukufana Nokunakwa Kwendandatho") is two such runs per shard; the driver handles it.
  *   - Grouped-query attention: query head h reads key/value head h / (Hq / Hkv).
  *
  * Running state between ring steps (fp32, caller-owned, persistent across calls):
@@ -58,9 +62,11 @@ extern "C" {
 #define RA_MASK_NONE 0
 #define RA_MASK_CAUSAL 1
 
-/* token layouts (ring_attn_local, ring_attn_plan) */
-#define RA_LAYOUT_CONTIGUOUS 0
-#define RA_LAYOUT_STRIPED 1
+/* token layouts (ring_attn_local, ring_attn_plan, ring_attn_visible_pairs) */
+#define RA_LAYOUT_CONTIGUOUS 0 /* shard i holds tokens [i*n, (i+1)*n) */
+#define RA_LAYOUT_STRIPED 1    /* token p on shard p mod P, local row p div P */
+#define RA_LAYOUT_ZIGZAG 2     /* 2P chunks of n/2 tokens; shard i holds chunk i, then chunk 2P-1-i
+                                  (n must be even) */
 
 /* status codes */
 #define RA_OK 0
@@ -123,7 +129,8 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  *                                    memory, or pinned host memory when kv_src_is_host != 0
  *   o   [n_local, B, n, Hq, D]       output (dtype), token-major, in shard order
  *   lse [n_local, B, Hq, n] fp32     log-sum-exp (may be NULL)
- *   layout                           RA_LAYOUT_CONTIGUOUS or RA_LAYOUT_STRIPED (sets positions)
+ *   layout                           RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED or RA_LAYOUT_ZIGZAG
+ *                                    (sets positions; zigzag needs n even)
  *   workspace                        device buffer of >= ring_attn_local_workspace_bytes(...) bytes:
  *                                    two staging slots of K and V for the local devices, and the
  *                                    fp32 running state
@@ -140,7 +147,8 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  * D = 128 kernel, a device that computes in step s hands its block to a local successor inside the
  * step-s kernel (the rows it stages for its own computation are stored into the successor's slot;
  * the host checks that every row of the block is staged, else it copies); every other hop is a
- * device-to-device (or, from pinned host memory, host-to-device) copy on copy_stream.  With a
+ * device-to-device (or, from pinned host memory, host-to-device) copy on copy_stream (always so under
+ * the zigzag layout, whose query chunks are folded as two units of n/2 rows).  With a
  * device-resident source a device's own block (step 0) is read in place.  Under RA_MASK_CAUSAL,
  * fully masked blocks are still passed on but not computed.  The last step of each device writes
  * o and lse directly.  The call returns after enqueueing; both streams are left ordered after all
@@ -159,6 +167,7 @@ size_t ring_attn_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hk
  * For each step s in [0, P) and each local device i in [dev0, dev0 + n_local), one row of 5 int32:
  *   { s, i, j = (i - s) mod P, staging slot (s mod 2), class }
  * class: 0 = fully masked (skipped), 1 = fully visible, 2 = partially visible (masked tiles).
+ * Returns RA_ERR_INVALID_ARG for an unknown layout, or zigzag with n odd.
  * out_rows (host) must hold P * n_local * 5 int32.
  */
 int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, int32_t* out_rows);

@@ -13,15 +13,15 @@ What is here, in float64 NumPy:
   for workloads too large for the full O(S^2) computation.
 * :func:`ring_replay` — the ring schedule with the online-softmax fold, in the pages' order and
   notation, used to check the method's own claims (exactness, arrival-order invariance) on the CPU.
-* :mod:`oracle.layout` — contiguous and striped token-to-shard assignment.
+* :mod:`oracle.layout` — contiguous, striped and zigzag token-to-shard assignment.
 
 Every function is pinned by CPU tests to facts outside itself (the pages' demonstration, library
 routines, closed forms, brute force); none is "parity unpinned".
 """
 from .attention import attention_reference, attention_rows, ring_replay
-from .layout import shard_positions, striped_permutation, contiguous_permutation
+from .layout import shard_positions, striped_permutation, contiguous_permutation, zigzag_permutation
 
 __all__ = [
     "attention_reference", "attention_rows", "ring_replay",
-    "shard_positions", "striped_permutation", "contiguous_permutation",
+    "shard_positions", "striped_permutation", "contiguous_permutation", "zigzag_permutation",
 ]

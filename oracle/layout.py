@@ -8,6 +8,12 @@ Striped sharding: tokens are dealt round-robin, token t goes to shard t mod P at
 t div P.  The Ultralytics glossary page "Ring Attention" (section "Como funciona a atenção em
 anel") says only that Striped Attention spreads the sequence's tokens evenly over the devices to
 fix causal imbalance; the round-robin deal is the plainest such even spread.
+
+Zigzag sharding: the page "Ukulandelana Ukuhambisana Nokunakwa Kwendandatho" (aiunderstanding.org,
+section "Ikusasa Lokulandelana Ukufana Nokunakwa Kwendandatho") names it beside striped attention
+as a way to rebalance the causal work, without defining it.  Reading taken: the sequence is cut
+into 2P equal chunks and shard i holds chunk i followed by chunk 2P-1-i, pairing an early chunk
+with a late one so that every shard sees the same number of visible keys.
 """
 from __future__ import annotations
 
@@ -25,6 +31,11 @@ def shard_positions(S: int, P: int, layout: str) -> np.ndarray:
         return i * n + r
     if layout == "striped":
         return r * P + i
+    if layout == "zigzag":
+        if n % 2:
+            raise ValueError("zigzag sharding needs an even number of tokens per shard")
+        c = n // 2
+        return np.where(r < c, i * c + r, (2 * P - 1 - i) * c + (r - c))
     raise ValueError(f"unknown layout {layout!r}")
 
 
@@ -35,6 +46,11 @@ def _perm(S: int, P: int, layout: str) -> np.ndarray:
 def contiguous_permutation(S: int, P: int) -> np.ndarray:
     """Identity: shard-major order equals token order."""
     return _perm(S, P, "contiguous")
+
+
+def zigzag_permutation(S: int, P: int) -> np.ndarray:
+    """perm such that x_sharded = x[:, perm] lists the zigzag shards in order (token axis 1)."""
+    return _perm(S, P, "zigzag")
 
 
 def striped_permutation(S: int, P: int) -> np.ndarray:

@@ -37,7 +37,7 @@ class Workload:
     Hkv: int
     D: int
     causal: bool
-    layout: str     # "contiguous" or "striped"
+    layout: str     # "contiguous", "striped" or "zigzag"
     dtype: str      # "f32" or "bf16"
     seed: int
     sigma: float = 1.0
@@ -68,6 +68,7 @@ WORKLOADS = {
     "causal_32k": Workload("causal_32k", 1, 32768, 8, 32, 32, 128, True, "contiguous", "bf16", 3000, 0.5),
     "causal_striped_64k": Workload("causal_striped_64k", 1, 65536, 8, 32, 8, 128, True, "striped", "bf16", 4000),
     "causal_contig_64k": Workload("causal_contig_64k", 1, 65536, 8, 32, 8, 128, True, "contiguous", "bf16", 4000),
+    "causal_zigzag_64k": Workload("causal_zigzag_64k", 1, 65536, 8, 32, 8, 128, True, "zigzag", "bf16", 4000),
     "causal_1m_shard": Workload("causal_1m_shard", 1, 1048576, 32, 8, 8, 128, True, "contiguous", "bf16", 5000,
                                 local_shard=31),
 }

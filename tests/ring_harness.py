@@ -88,7 +88,7 @@ def run_ring_local(q, k, v, *, P, causal, layout, dtype, dev0=0, n_local=None, s
                      device="cuda")
     copy_stream = torch.cuda.Stream() if two_streams else None
     ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=P, dev0=dev0, scale=scale, causal=causal,
-                       striped=(layout == "striped"), copy_stream=copy_stream)
+                       layout=layout, copy_stream=copy_stream)
     torch.cuda.synchronize()
     return out_to_f64(o), lse.cpu().numpy().astype(np.float64)
 

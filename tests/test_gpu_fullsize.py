@@ -72,7 +72,7 @@ def _run(w, q, k, v):
     ws = torch.empty(ra.ring_attn_local_workspace_bytes(w.P, n_local, B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
                      dtype=torch.uint8, device="cuda")
     ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=1.0 / math.sqrt(w.D), causal=w.causal,
-                       striped=(w.layout == "striped"), copy_stream=torch.cuda.Stream())
+                       layout=w.layout, copy_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     del tk, tv, ws
     return o, lse
@@ -125,16 +125,21 @@ def test_causal_64k_striped_gqa():
     _check("causal_striped_64k", 41)
 
 
+def test_causal_64k_zigzag_gqa():
+    _check("causal_zigzag_64k", 42)
+
+
 def test_one_device_share_of_1m_ring():
     _check("causal_1m_shard", 51)
 
 
-def test_striped_matches_contiguous_after_unpermuting():
-    """The same 64k causal GQA inputs under both shardings agree on every output element."""
+def test_striped_and_zigzag_match_contiguous_after_unpermuting():
+    """The same 64k causal GQA inputs under the three shardings agree on every output element."""
     ws_, wc = si.WORKLOADS["causal_striped_64k"], si.WORKLOADS["causal_contig_64k"]
+    wz = si.WORKLOADS["causal_zigzag_64k"]
     q, k, v = si.workload_qkv(ws_)
     outs = {}
-    for w in (ws_, wc):
+    for w in (ws_, wc, wz):
         o, lse = _run(w, q, k, v)
         pos = torch.from_numpy(_shard_positions(w).reshape(-1)).cuda()
         tok_o = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
@@ -144,8 +149,9 @@ def test_striped_matches_contiguous_after_unpermuting():
         outs[w.layout] = (tok_o, tok_l)
         del o, lse
         torch.cuda.empty_cache()
-    do = (outs["striped"][0].float() - outs["contiguous"][0].float()).abs().max().item()
-    dl = (outs["striped"][1] - outs["contiguous"][1]).abs().max().item()
-    print(f"[fullsize] striped vs contiguous 64k: max|dO|={do:.3g} max|dLSE|={dl:.3g}", flush=True)
-    assert math.isfinite(do) and math.isfinite(dl)
-    assert do <= TOL_BF16_O and dl <= TOL_BF16_LSE
+    for layout in ("striped", "zigzag"):
+        do = (outs[layout][0].float() - outs["contiguous"][0].float()).abs().max().item()
+        dl = (outs[layout][1] - outs["contiguous"][1]).abs().max().item()
+        print(f"[fullsize] {layout} vs contiguous 64k: max|dO|={do:.3g} max|dLSE|={dl:.3g}", flush=True)
+        assert math.isfinite(do) and math.isfinite(dl)
+        assert do <= TOL_BF16_O and dl <= TOL_BF16_LSE

@@ -96,6 +96,39 @@ def test_bf16_partly_local_ring(gpu_lib, causal, layout):
     assert max_err(got_o, ref_o) <= TOL_BF16_O and max_err(got_lse, ref_lse) <= TOL_BF16_LSE
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [40, 128])
+def test_fp32_zigzag_ring(gpu_lib, causal, D):
+    _check_ring(gpu_lib, 2, 4, 38, 3, 1, D, causal, "zigzag", "f32", 700 + D + causal)
+
+
+@pytest.mark.parametrize("causal,P,n", [(True, 4, 128), (True, 4, 200), (True, 8, 258), (False, 4, 130)])
+def test_bf16_mfma_zigzag_ring(gpu_lib, causal, P, n):
+    """Zigzag shards (chunks i and 2P-1-i): each device folds its two chunks as two row windows of
+    the step kernel, with ragged chunk lengths (100, 129, 65 rows) and two batch elements."""
+    _check_ring(gpu_lib, 2, P, n, 4, 2, 128, causal, "zigzag", "bf16", 720 + n)
+
+
+def test_bf16_zigzag_partly_local_and_many_devices(gpu_lib):
+    """Zigzag for devices 2..4 of a 6-device ring, and a 36-device ring whose 72 chunk units need
+    two launches per step."""
+    P, n, Hq, Hkv, D, dev0, n_local = 6, 160, 4, 2, 128, 2, 3
+    S = P * n
+    q, k, v = _inputs(1, S, Hq, Hkv, D, 760, "bf16")
+    pos = oracle.shard_positions(S, P, "zigzag")
+    q_local = q[:, pos[dev0:dev0 + n_local].reshape(-1)]
+    o, lse = run_ring_local(q_local, k, v, P=P, causal=True, layout="zigzag", dtype="bf16", dev0=dev0,
+                            n_local=n_local)
+    toks = pos[dev0:dev0 + n_local]
+    rows = np.array([[0, h, int(toks[t, r])] for t in range(n_local) for h in range(Hq) for r in range(n)])
+    ref_o, ref_lse = oracle.attention_rows(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"), rows,
+                                           causal=True)
+    got_o = np.concatenate([o[t, 0].transpose(1, 0, 2).reshape(-1, D) for t in range(n_local)])
+    got_lse = np.concatenate([lse[t, 0].reshape(-1) for t in range(n_local)])
+    assert max_err(got_o, ref_o) <= TOL_BF16_O and max_err(got_lse, ref_lse) <= TOL_BF16_LSE
+    _check_ring(gpu_lib, 1, 36, 64, 2, 1, 128, True, "zigzag", "bf16", 770)
+
+
 def test_bf16_mfma_ring_gqa_striped_p8(gpu_lib):
     _check_ring(gpu_lib, 1, 8, 192, 8, 2, 128, True, "striped", "bf16", 300)
 

@@ -80,6 +80,26 @@ def test_visible_pairs_match_brute_force_and_closed_forms(P, n):
         assert ra.ring_attn_visible_pairs(P, n, 0, P - 1, causal=False, striped=striped) == n * n
 
 
+@pytest.mark.parametrize("P,n", [(1, 2), (4, 8), (8, 16), (32, 4)])
+def test_zigzag_plan_and_visible_pairs(P, n):
+    S, c = P * n, n // 2
+    pos = oracle.shard_positions(S, P, "zigzag")
+    plan = ra.ring_attn_plan(P, 0, P, n, causal=True, layout="zigzag")
+    for s, i, j, slot, cls in plan:
+        assert j == (i - s) % P and slot == s % 2
+        assert cls == 2  # each pair mixes visible and masked keys
+    for i in range(P):
+        row = [ra.ring_attn_visible_pairs(P, n, i, j, causal=True, layout="zigzag") for j in range(P)]
+        assert row == [int((pos[j][None, :] <= pos[i][:, None]).sum()) for j in range(P)]
+        assert row == [c * c + c * (c + 1) if j == i else 2 * c * c for j in range(P)]
+    assert ra.ring_attn_visible_pairs(P, n, 0, P - 1, causal=False, layout="zigzag") == n * n
+    L = ra.lib()
+    buf = (ctypes.c_int32 * (5 * P * P))()
+    assert L.ring_attn_plan(P, 0, P, n + 1, 1, 2, buf) == -1        # zigzag needs n even
+    assert L.ring_attn_visible_pairs(P, n + 1, 1, 2, 0, 0) == -1
+    assert L.ring_attn_plan(P, 0, P, n, 1, 3, buf) == -1            # unknown layout
+
+
 def test_causal_critical_path_ratio():
     """Per-step barrier: sum over steps of the busiest device; contiguous/striped -> (2P-1)/P."""
     for P, n in ((8, 4096), (32, 32768)):

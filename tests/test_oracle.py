@@ -242,15 +242,28 @@ def test_random_arrival_orders_p8():
         assert np.abs(np.concatenate(outs) - ref2[0, :, 0]).max() < 1e-12
 
 
-def test_striped_equals_contiguous_after_unpermuting():
+def test_zigzag_layout_table():
+    # written out by hand: 8 chunks of 3 tokens; shard i holds chunk i, then chunk 7 - i
+    expected = [[0, 1, 2, 21, 22, 23],
+                [3, 4, 5, 18, 19, 20],
+                [6, 7, 8, 15, 16, 17],
+                [9, 10, 11, 12, 13, 14]]
+    assert oracle.shard_positions(24, 4, "zigzag").tolist() == expected
+    assert sorted(oracle.zigzag_permutation(24, 4).tolist()) == list(range(24))
+    with pytest.raises(ValueError):
+        oracle.shard_positions(20, 4, "zigzag")  # 5 tokens per shard cannot be split into two chunks
+
+
+@pytest.mark.parametrize("layout", ["striped", "zigzag"])
+def test_striped_equals_contiguous_after_unpermuting(layout):
     P, n, D, H = 4, 6, 8, 2
     S = P * n
     q = _rand((1, S, H, D), 91)
     k = _rand((1, S, 1, D), 92)
     v = _rand((1, S, 1, D), 93)
     ref, ref_lse = oracle.attention_reference(q, k, v, causal=True)
-    perm = oracle.striped_permutation(S, P)
-    pos = oracle.shard_positions(S, P, "striped")
+    perm = oracle.shard_positions(S, P, layout).reshape(-1)
+    pos = oracle.shard_positions(S, P, layout)
     for h in range(H):
         outs, lses = oracle.ring_replay(_blocks(q[0, perm, h], P), _blocks(k[0, perm, 0], P), _blocks(v[0, perm, 0], P),
                                         scale=1 / math.sqrt(D), causal=True, q_pos_blocks=pos, k_pos_blocks=pos)
@@ -261,7 +274,7 @@ def test_striped_equals_contiguous_after_unpermuting():
         lse_u = np.empty(S)
         lse_u[perm] = np.concatenate(lses)
         assert np.abs(lse_u - ref_lse[0, h]).max() < 1e-12
-    # the striped layout really is a different token order (sanity: not the identity for P > 1)
+    # the layout really is a different token order (sanity: not the identity for P > 1)
     assert not np.array_equal(perm, np.arange(S))
 
 
@@ -318,6 +331,17 @@ def test_visible_pair_counts_closed_forms(P, n):
         return sum(max(_pairs(pos[i], pos[(i - s) % P]) for i in range(P)) for s in range(P))
     assert crit("contiguous") == n * (n + 1) // 2 + (P - 1) * n * n
     assert crit("striped") == P * n * (n + 1) // 2
+    if n % 2 == 0:
+        # zigzag: shard i's early chunk i sees chunks 0..i, its late chunk 2P-1-i sees 0..2P-1-i;
+        # every shard gets (2P-1) c^2 + c (c+1) pairs, and in each step every shard does the same
+        # work (c^2 + c (c+1) on its own block, 2 c^2 on any other), so the critical path is that too
+        c = n // 2
+        pos = oracle.shard_positions(S, P, "zigzag")
+        for i in range(P):
+            assert sum(_pairs(pos[i], pos[j]) for j in range(P)) == (2 * P - 1) * c * c + c * (c + 1)
+            for j in range(P):
+                assert _pairs(pos[i], pos[j]) == (c * c + c * (c + 1) if j == i else 2 * c * c)
+        assert crit("zigzag") == (2 * P - 1) * c * c + c * (c + 1)
 
 
 def test_workload_flop_counts():
