@@ -153,23 +153,25 @@ def run_workload(w, steps, warmup, measure_clock=True):
     log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
         f"step kernels {kernel_total_ms:.3f} ms ({achieved:.1f} TFLOP/s), per step "
         + ", ".join(f"{x:.3f}" for x in launch_ms))
-    sclk = sample_sclk(call, torch) if measure_clock else None
+    sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
     if sclk:
-        log(f"{w.name}: GFX clock under this load {sclk:.0f} MHz")
+        log(f"{w.name}: GFX clock under this load {sclk:.0f} MHz (GPU busy for ~{100 * busy:.0f}% of the sampling)")
     res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
                ms_min=per_call[0], tflops=tflops,
                flops=flops, kernel_ms=kernel_total_ms, kernel_tflops=achieved, launch_ms=launch_ms,
-               launch_flops=per_launch, sclk_mhz=sclk)
+               launch_flops=per_launch, sclk_mhz=sclk, sclk_busy=busy)
     del tq, tk, tv, o, lse, ws
     torch.cuda.empty_cache()
     return res
 
 
-def sample_sclk(call, torch, seconds=1.2):
-    """Median GFX clock (MHz) reported by amdsmi while the same calls keep the GPU busy: a background
-    thread samples every 10 ms while this thread keeps enqueuing calls for `seconds` (the queue
-    stays full, so every sample is taken under the load); the first third of the samples is dropped
-    (the reading lags).  None if amdsmi is unavailable."""
+def sample_sclk(call, torch, ms_per_call, seconds=1.2):
+    """(median GFX clock in MHz, GPU busy fraction) while the same calls keep the GPU busy: a
+    background thread reads amdsmi every 10 ms while this thread keeps enqueuing calls for
+    `seconds`; the first third of the readings is dropped (the reading lags).  The busy fraction is
+    the calls' GPU time (at the timed ms per call) over the wall time until they all completed; well
+    below 1 means the host could not keep the queue full and the reading is not one under load.
+    (None, None) if amdsmi is unavailable."""
     import threading
 
     try:
@@ -178,7 +180,7 @@ def sample_sclk(call, torch, seconds=1.2):
         h = amdsmi.amdsmi_get_processor_handles()[0]
     except Exception as e:  # pragma: no cover
         log(f"amdsmi unavailable ({e!r}); no clock reading")
-        return None
+        return None, None
     samples, stop = [], threading.Event()
 
     def sampler():
@@ -191,18 +193,22 @@ def sample_sclk(call, torch, seconds=1.2):
 
     th = threading.Thread(target=sampler, daemon=True)
     try:
+        torch.cuda.synchronize()
         th.start()
         t0 = time.time()
+        n_calls = 0
         while time.time() - t0 < seconds:
             call()
+            n_calls += 1
         stop.set()
         th.join()
         torch.cuda.synchronize()
+        busy = min(1.0, n_calls * ms_per_call * 1e-3 / (time.time() - t0))
         kept = sorted(samples[len(samples) // 3:])
-        return float(kept[len(kept) // 2]) if kept else None
+        return (float(kept[len(kept) // 2]) if kept else None), busy
     except Exception as e:  # pragma: no cover
         log(f"clock sampling failed ({e!r})")
-        return None
+        return None, None
     finally:
         stop.set()
         amdsmi.amdsmi_shut_down()
@@ -309,7 +315,7 @@ def main():
                        "warmup": r["warmup"], "ms_per_step": r["ms"],
                        "ms_per_step_median": r["ms_median"], "ms_per_step_min": r["ms_min"],
                        "pct_of_peak": 100 * r["tflops"] / PEAK_BF16_TFLOPS, "step_kernel_tflops": r["kernel_tflops"],
-                       "sclk_mhz": r["sclk_mhz"],
+                       "sclk_mhz": r["sclk_mhz"], "sclk_gpu_busy": r["sclk_busy"],
                        "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"]) if r["sclk_mhz"] else None),
                        "causal": si.WORKLOADS[name].causal, "layout": si.WORKLOADS[name].layout})
 
@@ -334,6 +340,7 @@ def main():
         "pct_of_peak": 100 * main_res["tflops"] / PEAK_BF16_TFLOPS,
         "ms_per_step_median": main_res["ms_median"], "ms_per_step_min": main_res["ms_min"],
         "sclk_mhz": main_res["sclk_mhz"],
+        "sclk_gpu_busy": main_res["sclk_busy"],
         "pct_of_peak_at_sclk": (100 * main_res["tflops"] / clock_peak(main_res["sclk_mhz"])
                                 if main_res["sclk_mhz"] else None),
         "roofline": roof, "cpu_baseline": cpu, "extra": extras,
