@@ -13,15 +13,20 @@ What is here, in float64 NumPy:
   for workloads too large for the full O(S^2) computation.
 * :func:`ring_replay` — the ring schedule with the online-softmax fold, in the pages' order and
   notation, used to check the method's own claims (exactness, arrival-order invariance) on the CPU.
+* :func:`attention_backward_reference`, :func:`attention_backward_rows` — the gradients dQ, dK, dV
+  of the same definition for an output gradient dO (chain rule written out; the pages use the ring
+  for training but do not spell out its backward pass).
 * :mod:`oracle.layout` — contiguous, striped and zigzag token-to-shard assignment.
 
 Every function is pinned by CPU tests to facts outside itself (the pages' demonstration, library
 routines, closed forms, brute force); none is "parity unpinned".
 """
 from .attention import attention_reference, attention_rows, ring_replay
+from .backward import attention_backward_reference, attention_backward_rows
 from .layout import shard_positions, striped_permutation, contiguous_permutation, zigzag_permutation
 
 __all__ = [
     "attention_reference", "attention_rows", "ring_replay",
+    "attention_backward_reference", "attention_backward_rows",
     "shard_positions", "striped_permutation", "contiguous_permutation", "zigzag_permutation",
 ]
