@@ -7,7 +7,8 @@ There is no CPU fallback: the functions raise if the library is not built or no 
 """
 from ._binding import (  # noqa: F401
     RA_BF16, RA_F32, RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG, RA_MASK_CAUSAL, RA_MASK_NONE,
-    RA_MAX_D, RA_MAX_DEV, RA_STEP_INIT, RingAttnError, HipEvent, lib, lib_path, ring_attn_finalize, ring_attn_local,
+    RA_MAX_D, RA_MAX_DEV, RA_STEP_INIT, RA_BWD_INIT_DQ, RA_BWD_INIT_DKV, RingAttnError, HipEvent, lib, lib_path, ring_attn_finalize, ring_attn_local,
     ring_attn_local_workspace_bytes, ring_attn_plan, ring_attn_step, ring_attn_strerror, ring_attn_visible_pairs,
+    ring_attn_bwd_prep, ring_attn_bwd_step, ring_attn_bwd_local, ring_attn_bwd_local_workspace_bytes,
     EXPORTED_SYMBOLS,
 )

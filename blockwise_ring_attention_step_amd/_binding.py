@@ -22,12 +22,16 @@ def _layout_code(layout, striped):
     if layout not in _LAYOUTS or (striped and layout != "striped"):
         raise ValueError(f"unknown or conflicting layout {layout!r}")
     return _LAYOUTS[layout]
+
+
 RA_STEP_INIT = 1
+RA_BWD_INIT_DQ, RA_BWD_INIT_DKV = 1, 2
 RA_MAX_DEV, RA_MAX_D = 64, 128
 
 EXPORTED_SYMBOLS = (
     "ring_attn_step", "ring_attn_finalize", "ring_attn_local", "ring_attn_local_workspace_bytes",
     "ring_attn_plan", "ring_attn_visible_pairs", "ring_attn_strerror",
+    "ring_attn_bwd_prep", "ring_attn_bwd_step", "ring_attn_bwd_local", "ring_attn_bwd_local_workspace_bytes",
 )
 
 _lib = None
@@ -67,6 +71,16 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_plan.restype = i32
     L.ring_attn_visible_pairs.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ring_attn_visible_pairs.restype = i64
+    L.ring_attn_bwd_prep.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.ring_attn_bwd_prep.restype = i32
+    L.ring_attn_bwd_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                     i32, p64, i64, p64, i64, i32, vp]
+    L.ring_attn_bwd_step.restype = i32
+    L.ring_attn_bwd_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      f32, i32, i32, vp, sz, vp, vp]
+    L.ring_attn_bwd_local.restype = i32
+    L.ring_attn_bwd_local_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.ring_attn_bwd_local_workspace_bytes.restype = sz
     L.ring_attn_strerror.argtypes = [i32]
     L.ring_attn_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -193,6 +207,47 @@ def ring_attn_visible_pairs(P, n, i, j, *, causal=False, striped=False, layout=N
     if r < 0:
         raise RingAttnError("ring_attn_visible_pairs", -1)
     return int(r)
+
+
+def ring_attn_bwd_prep(o, dout, lse, delta, lse2, *, stream=None):
+    """delta = sum_d dout * o and lse2 = log2(e) * lse; o, dout [n_dev, B, Nq, Hq, D], the rest [n_dev, B, Hq, Nq]."""
+    n_dev, B, Nq, Hq, D = o.shape
+    rc = lib().ring_attn_bwd_prep(_ptr(o), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(lse2), n_dev, B, Hq, Nq, D,
+                                  _dtype_code(o), _stream(stream))
+    _check("ring_attn_bwd_prep", rc)
+
+
+def ring_attn_bwd_step(q, k, v, dout, lse2, delta, dq, dk, dv, *, scale, causal=False, q_off=None, q_stride=1,
+                       k_off=None, k_stride=1, init_dq=False, init_dkv=False, stream=None):
+    """Add the gradient contributions of the pairs (q[t], k[t], v[t]) to dq[t], dk[t], dv[t] (fp32)."""
+    n_dev, B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[2], k.shape[3]
+    flags = (RA_BWD_INIT_DQ if init_dq else 0) | (RA_BWD_INIT_DKV if init_dkv else 0)
+    rc = lib().ring_attn_bwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse2), _ptr(delta), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), n_dev, B, Hq, Hkv, Nq, Nk, D, _dtype_code(q), float(scale),
+                                  RA_MASK_CAUSAL if causal else RA_MASK_NONE, _i64_array(q_off), int(q_stride),
+                                  _i64_array(k_off), int(k_stride), flags, _stream(stream))
+    _check("ring_attn_bwd_step", rc)
+
+
+def ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype):
+    return int(lib().ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype))
+
+
+def ring_attn_bwd_local(q_local, k_src, v_src, o_local, dout_local, lse_local, dq_local, dk, dv, workspace, *, P,
+                        dev0, scale, causal=False, layout=None, striped=False, compute_stream=None, copy_stream=None):
+    """Backward ring for the local devices [dev0, dev0 + n_local): dq_local [n_local, B, n, Hq, D] and
+    dk, dv [P, B, n, Hkv, D] (fp32), from the forward's inputs, output, log-sum-exp and the output gradient."""
+    n_local, B, n, Hq, D = q_local.shape
+    Hkv = k_src.shape[3]
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    rc = lib().ring_attn_bwd_local(_ptr(q_local), _ptr(k_src), _ptr(v_src), _ptr(o_local), _ptr(dout_local),
+                                   _ptr(lse_local), _ptr(dq_local), _ptr(dk), _ptr(dv), P, dev0, n_local, B, Hq, Hkv,
+                                   n, D, _dtype_code(q_local), float(scale), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+                                   _layout_code(layout, striped), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), cs, xs)
+    _check("ring_attn_bwd_local", rc)
 
 
 _HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000

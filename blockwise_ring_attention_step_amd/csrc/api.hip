@@ -592,4 +592,296 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   return RA_OK;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Backward pass of the ring (gradients of exact attention).
+
+int ring_attn_bwd_prep(const void* o, const void* dout, const float* lse, float* delta, float* lse2, int n_dev, int B,
+                       int Hq, int Nq, int D, int dtype, void* stream) {
+  if (n_dev < 1 || n_dev > RA_MAX_DEV || B < 1 || Hq < 1 || Nq < 0 || D < 1) return RA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return RA_ERR_INVALID_ARG;
+  if (D > RA_MAX_D) return RA_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)n_dev * B * Hq * Nq;
+  if (rows == 0) return RA_OK;
+  if (!o || !dout || !lse || !delta || !lse2) return RA_ERR_INVALID_ARG;
+  const size_t in_bytes = rows * D * elem_size(dtype);
+  const void* ins[3] = {o, dout, lse};
+  const size_t in_sz[3] = {in_bytes, in_bytes, rows * 4};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(delta, rows * 4, ins[a], in_sz[a]) || overlaps(lse2, rows * 4, ins[a], in_sz[a])) return RA_ERR_INVALID_ARG;
+  if (overlaps(delta, rows * 4, lse2, rows * 4)) return RA_ERR_INVALID_ARG;
+  return hip_status(ra::launch_bwd_prep(o, dout, lse, delta, lse2, n_dev, B, Hq, Nq, D, dtype, (hipStream_t)stream));
+}
+
+int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                       const float* delta, float* dq, float* dk, float* dv, int n_dev, int B, int Hq, int Hkv, int Nq,
+                       int Nk, int D, int dtype, float scale, int mask, const int64_t* q_off, int64_t q_stride,
+                       const int64_t* k_off, int64_t k_stride, int flags, void* stream) {
+  const Shape sh{n_dev, B, Hq, Hkv, Nq, Nk, D, dtype};
+  int rc = validate_shape(sh);
+  if (rc != RA_OK) return rc;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
+  if (flags & ~(RA_BWD_INIT_DQ | RA_BWD_INIT_DKV)) return RA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
+  if (!uses_mfma_kernel(dtype, D)) return RA_ERR_UNSUPPORTED;
+  const bool causal = mask == RA_MASK_CAUSAL;
+  if (causal && (!q_off || !k_off || q_stride <= 0 || k_stride <= 0)) return RA_ERR_INVALID_ARG;
+  const size_t qrows = (size_t)n_dev * B * Nq * Hq, krows = (size_t)n_dev * B * Nk * Hkv;
+  if (qrows + krows == 0) return RA_OK;
+  if ((qrows > 0 && (!q || !dout || !lse2 || !delta || !dq)) || (krows > 0 && (!k || !v || !dk || !dv)))
+    return RA_ERR_INVALID_ARG;
+  // the gradients are written: they may not alias the inputs or each other
+  const void* outs[3] = {dq, dk, dv};
+  const size_t out_sz[3] = {qrows * D * 4, krows * D * 4, krows * D * 4};
+  const void* ins[6] = {q, k, v, dout, lse2, delta};
+  const size_t in_sz[6] = {qrows * D * 2, krows * D * 2, krows * D * 2, qrows * D * 2, qrows * 4, qrows * 4};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_sz[a], ins[b], in_sz[b])) return RA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return RA_ERR_INVALID_ARG;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  ra::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.lse2 = lse2;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = p.NqTot = Nq;
+  p.Nk = p.NkTot = Nk;
+  p.D = D;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = (float)(scale * kLog2e);
+  p.q_stride = causal ? q_stride : 1;
+  p.k_stride = causal ? k_stride : 1;
+  for (int t = 0; t < n_dev; ++t) {
+    const int64_t qo = q_off ? q_off[t] : 0, ko = k_off ? k_off[t] : 0;
+    if (classify(causal, qo, p.q_stride, Nq, ko, p.k_stride, Nk) == 0) {
+      // nothing visible: only an initialisation to do
+      const size_t qn = (size_t)B * Nq * Hq * D, kn = (size_t)B * Nk * Hkv * D;
+      hipError_t e = hipSuccess;
+      if (flags & RA_BWD_INIT_DQ) e = ra::launch_zero_f32(dq + t * qn, qn, st);
+      if (e == hipSuccess && (flags & RA_BWD_INIT_DKV)) e = ra::launch_zero_f32(dk + t * kn, kn, st);
+      if (e == hipSuccess && (flags & RA_BWD_INIT_DKV)) e = ra::launch_zero_f32(dv + t * kn, kn, st);
+      if (e != hipSuccess) return RA_ERR_HIP;
+      continue;
+    }
+    const int x = p.n_launch++;
+    p.qslot[x] = p.kvslot[x] = p.gslot[x] = t;
+    p.q_row0[x] = 0;
+    p.nk[x] = Nk;
+    p.q_off[x] = qo;
+    p.k_off[x] = ko;
+    p.flags[x] = (uint8_t)(((flags & RA_BWD_INIT_DQ) ? ra::kBwdInitDq : 0) |
+                           ((flags & RA_BWD_INIT_DKV) ? ra::kBwdInitDkv : 0));
+  }
+  if (p.n_launch == 0) return RA_OK;
+  rc = hip_status(ra::launch_bwd_dq_bf16_d128(p, st));
+  if (rc != RA_OK) return rc;
+  return hip_status(ra::launch_bwd_dkv_bf16_d128(p, st));
+}
+
+size_t ring_attn_bwd_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype) {
+  if (P < 1 || P > RA_MAX_DEV || n_local < 1 || n_local > P || B < 1 || Hq < 1 || Hkv < 1 || n < 0 || D < 1 ||
+      D > RA_MAX_D || Hq % Hkv || !valid_dtype(dtype))
+    return 0;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t blk = (size_t)B * n * Hkv * D * elem_size(dtype);
+  const size_t rows = (size_t)n_local * B * Hq * n;
+  return 4 * up((size_t)n_local * blk) + 2 * up(rows * 4);
+}
+
+int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_src, const void* o_local,
+                        const void* dout_local, const float* lse_local, float* dq_local, float* dk, float* dv, int P,
+                        int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype, float scale, int mask,
+                        int layout, void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream) {
+  if (P < 1 || P > RA_MAX_DEV || dev0 < 0 || dev0 >= P || n_local < 1 || dev0 + n_local > P) return RA_ERR_INVALID_ARG;
+  const Shape sh{n_local, B, Hq, Hkv, n, n, D, dtype};
+  int rc = validate_shape(sh);
+  if (rc != RA_OK) return rc;
+  if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
+  if (!valid_layout(layout)) return RA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
+  if (!uses_mfma_kernel(dtype, D) || layout == RA_LAYOUT_ZIGZAG) return RA_ERR_UNSUPPORTED;
+  if (n == 0) return RA_OK;
+  if (!q_local || !k_src || !v_src || !o_local || !dout_local || !lse_local || !dq_local || !dk || !dv || !workspace)
+    return RA_ERR_INVALID_ARG;
+  const size_t need = ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype);
+  if (need == 0) return RA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return RA_ERR_WORKSPACE;
+
+  const size_t es = elem_size(dtype);
+  const size_t blk = (size_t)B * n * Hkv * D * es;  // one device's K (or V) block
+  const size_t rows = (size_t)n_local * B * Hq * n;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* ws = (char*)workspace;
+  char* stage_k[2] = {ws, ws + up((size_t)n_local * blk)};
+  char* stage_v[2] = {ws + 2 * up((size_t)n_local * blk), ws + 3 * up((size_t)n_local * blk)};
+  float* delta = (float*)(ws + 4 * up((size_t)n_local * blk));
+  float* lse2 = (float*)((char*)delta + up(rows * 4));
+  // outputs may not alias the inputs, the workspace or each other
+  const size_t q_bytes = rows * D * es, src_bytes = (size_t)P * blk;
+  const size_t dq_bytes = rows * D * 4, dkv_bytes = (size_t)P * B * n * Hkv * D * 4;
+  const void* ins[7] = {q_local, k_src, v_src, o_local, dout_local, lse_local, workspace};
+  const size_t in_sz[7] = {q_bytes, src_bytes, src_bytes, q_bytes, q_bytes, rows * 4, need};
+  const void* outs[3] = {dq_local, dk, dv};
+  const size_t out_sz[3] = {dq_bytes, dkv_bytes, dkv_bytes};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 7; ++b)
+      if (overlaps(outs[a], out_sz[a], ins[b], in_sz[b])) return RA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return RA_ERR_INVALID_ARG;
+  }
+  for (int b = 0; b < 6; ++b)
+    if (overlaps(workspace, need, ins[b], in_sz[b])) return RA_ERR_INVALID_ARG;
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t xs = (hipStream_t)copy_stream;
+  const bool causal = mask == RA_MASK_CAUSAL;
+  const int64_t st = layout_stride(layout, P);
+
+  // schedule: class of every (step, device); first computed step of each device's query gradient
+  // and first visit of each block's key/value gradient
+  std::vector<int> cls((size_t)P * n_local);
+  std::vector<int> dq_first(n_local, -1), dkv_first(P, -1);
+  std::vector<uint8_t> first_flags((size_t)P * n_local, 0);
+  for (int s = 0; s < P; ++s)
+    for (int t = 0; t < n_local; ++t) {
+      const int i = dev0 + t, j = ((i - s) % P + P) % P;
+      const int c = classify(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n);
+      cls[(size_t)s * n_local + t] = c;
+      if (c == 0) continue;
+      uint8_t f = 0;
+      if (dq_first[t] < 0) {
+        dq_first[t] = s;
+        f |= ra::kBwdInitDq;
+      }
+      if (dkv_first[j] < 0) {
+        dkv_first[j] = s;
+        f |= ra::kBwdInitDkv;
+      }
+      first_flags[(size_t)s * n_local + t] = f;
+    }
+
+  hipEvent_t ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr}, ev_fork = nullptr;
+  auto cleanup = [&]() {
+    for (int a = 0; a < 2; ++a) {
+      if (ev_copy[a]) (void)hipEventDestroy(ev_copy[a]);
+      if (ev_comp[a]) (void)hipEventDestroy(ev_comp[a]);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+  };
+#define RA_CHECK(x)            \
+  do {                         \
+    hipError_t e_ = (x);       \
+    if (e_ != hipSuccess) {    \
+      cleanup();               \
+      return RA_ERR_HIP;       \
+    }                          \
+  } while (0)
+  for (int a = 0; a < 2; ++a) {
+    RA_CHECK(hipEventCreateWithFlags(&ev_copy[a], hipEventDisableTiming));
+    RA_CHECK(hipEventCreateWithFlags(&ev_comp[a], hipEventDisableTiming));
+  }
+  RA_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
+  const bool two_streams = xs != cs;
+  if (two_streams) {
+    RA_CHECK(hipEventRecord(ev_fork, cs));
+    RA_CHECK(hipStreamWaitEvent(xs, ev_fork, 0));
+  }
+  const char* ksrc = (const char*)k_src;
+  const char* vsrc = (const char*)v_src;
+  // the blocks of step s >= 1 arrive by copy into staging slot s & 1 (block (i - s) mod P of every
+  // local device, copied from its source shard); step 0 reads each device's own shard in place
+  auto enqueue_hop = [&](int s) -> hipError_t {
+    const int sl = s & 1;
+    for (int t = 0; t < n_local;) {
+      const int j0 = ((dev0 + t - s) % P + P) % P;
+      int t2 = t + 1;
+      while (t2 < n_local && ((dev0 + t2 - s) % P + P) % P == j0 + (t2 - t)) ++t2;  // contiguous source run
+      const size_t bytes = (size_t)(t2 - t) * blk;
+      hipError_t e = hipMemcpyAsync(stage_k[sl] + t * blk, ksrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(stage_v[sl] + t * blk, vsrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
+      if (e != hipSuccess) return e;
+      t = t2;
+    }
+    return hipSuccess;
+  };
+
+  RA_CHECK(ra::launch_bwd_prep(o_local, dout_local, lse_local, delta, lse2, n_local, B, Hq, n, D, dtype, cs));
+  for (int s = 0; s < P; ++s) {
+    if (s + 1 < P) {  // copies for step s+1, into the slot that step s-1 read
+      if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
+      RA_CHECK(enqueue_hop(s + 1));
+      RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
+    }
+    if (s >= 1) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
+    ra::BwdParams p{};
+    p.q = q_local;
+    p.k = s > 0 ? (const void*)stage_k[s & 1] : (const void*)(ksrc + (size_t)dev0 * blk);
+    p.v = s > 0 ? (const void*)stage_v[s & 1] : (const void*)(vsrc + (size_t)dev0 * blk);
+    p.dout = dout_local;
+    p.lse2 = lse2;
+    p.delta = delta;
+    p.dq = dq_local;
+    p.dk = dk;
+    p.dv = dv;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = p.NqTot = n;
+    p.Nk = p.NkTot = n;
+    p.D = D;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.scale_log2 = (float)(scale * kLog2e);
+    p.q_stride = st;
+    p.k_stride = st;
+    for (int t = 0; t < n_local; ++t) {
+      if (cls[(size_t)s * n_local + t] == 0) continue;
+      const int i = dev0 + t, j = ((i - s) % P + P) % P;
+      const int x = p.n_launch++;
+      p.qslot[x] = p.kvslot[x] = t;
+      p.gslot[x] = j;
+      p.q_row0[x] = 0;
+      p.nk[x] = n;
+      p.q_off[x] = block_offset(layout, P, n, i);
+      p.k_off[x] = block_offset(layout, P, n, j);
+      p.flags[x] = first_flags[(size_t)s * n_local + t];
+    }
+    if (p.n_launch > 0) {
+      RA_CHECK(ra::launch_bwd_dq_bf16_d128(p, cs));
+      RA_CHECK(ra::launch_bwd_dkv_bf16_d128(p, cs));
+    }
+    if (s + 2 < P) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+  }
+  // gradients nothing contributed to: zero
+  const size_t qn = (size_t)B * n * Hq * D, kn = (size_t)B * n * Hkv * D;
+  for (int t = 0; t < n_local; ++t)
+    if (dq_first[t] < 0) RA_CHECK(ra::launch_zero_f32(dq_local + t * qn, qn, cs));
+  for (int j = 0; j < P; ++j)
+    if (dkv_first[j] < 0) {
+      RA_CHECK(ra::launch_zero_f32(dk + j * kn, kn, cs));
+      RA_CHECK(ra::launch_zero_f32(dv + j * kn, kn, cs));
+    }
+  if (two_streams) {
+    RA_CHECK(hipEventRecord(ev_copy[0], xs));
+    RA_CHECK(hipStreamWaitEvent(cs, ev_copy[0], 0));
+    RA_CHECK(hipEventRecord(ev_comp[0], cs));
+    RA_CHECK(hipStreamWaitEvent(xs, ev_comp[0], 0));
+  }
+  cleanup();
+#undef RA_CHECK
+  return RA_OK;
+}
+
 }  // extern "C"

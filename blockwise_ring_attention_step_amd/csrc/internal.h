@@ -52,6 +52,43 @@ struct StepParams {
   void* fwd_v[RA_MAX_DEV];
 };
 
+// Per-slot flags of a backward step launch.
+enum : uint8_t {
+  kBwdInitDq = 1,   // overwrite this slot's query-gradient rows instead of adding to them
+  kBwdInitDkv = 2,  // overwrite this slot's key/value-gradient rows instead of adding to them
+};
+
+// Everything one backward step launch needs (both kernels of it).  Launch slot t pairs the query
+// rows [q_row0[t], q_row0[t] + Nq) of device qslot[t] (q, dout, lse2, delta, dq at that index of
+// their leading dimension; NqTot rows per (device, batch)) with the keys [0, nk[t]) of the block
+// in kvslot[t] of k and v, whose gradients accumulate at index gslot[t] of dk and dv (NkTot rows per
+// (block, batch)).  Positions and masking as in StepParams.
+struct BwdParams {
+  const void* q;       // [.., B, NqTot, Hq, D]
+  const void* k;       // [.., B, NkTot, Hkv, D]
+  const void* v;
+  const void* dout;    // like q: gradient of the attention output
+  const float* lse2;   // [.., B, Hq, NqTot]: log2 of sum_u 2^(x_u), x = log2(e) * scale * q.k (forward)
+  const float* delta;  // [.., B, Hq, NqTot]: sum_d dout * out of the row
+  float* dq;           // [.., B, NqTot, Hq, D] fp32
+  float* dk;           // [.., B, NkTot, Hkv, D] fp32
+  float* dv;
+  int n_launch;
+  int B, Hq, Hkv, Nq, Nk, NqTot, NkTot, D;  // Nq: query rows per slot; Nk: the largest nk[t]
+  int causal;
+  float scale, scale_log2;
+  int64_t q_stride, k_stride;
+  int groups, groups_per_xcd, n_qtiles, n_ktiles;  // filled in by the launchers
+  int qslot[RA_MAX_DEV];
+  int kvslot[RA_MAX_DEV];
+  int gslot[RA_MAX_DEV];
+  int q_row0[RA_MAX_DEV];
+  int nk[RA_MAX_DEV];
+  int64_t q_off[RA_MAX_DEV];
+  int64_t k_off[RA_MAX_DEV];
+  uint8_t flags[RA_MAX_DEV];
+};
+
 // Work geometry of the bf16 D=128 step kernel that the host also needs (the in-step hop): query rows
 // per workgroup and keys per tile.
 constexpr int kMfmaRowsPerWg = 256;
@@ -62,6 +99,12 @@ constexpr int kMfmaKeysPerTile = 64;
 hipError_t launch_step_mfma_bf16_d128(const StepParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start,
                                hipEvent_t ev_stop);
+hipError_t launch_bwd_dq_bf16_d128(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dkv_bf16_d128(const BwdParams& p, hipStream_t stream);
+// delta[row] = sum_d dout * out and lse2[row] = log2(e) * lse[row], rows of [n_dev, B, Hq, Nq]
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2, int n_dev,
+                           int B, int Hq, int Nq, int D, int dtype, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
 hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
                            int B, int Hq, int Nq, int D, int out_dtype, hipStream_t stream);
 hipError_t launch_init_state(float* o_acc, float* m, float* l, int n_dev_total, const int* slots, int n_slots,

@@ -40,51 +40,31 @@
 // 4 chunks) then hit distinct banks.
 #include <hip/hip_ext.h>
 
+#include "gfx950_tile.h"
 #include "internal.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+using namespace tile;
 
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;              // query rows per workgroup
 constexpr int kBc = 64;                       // keys per tile
-constexpr int kRowBytes = kD * 2;             // one key row of K or V in LDS
 constexpr int kTileBytes = kBc * kRowBytes;   // 16 KiB
 constexpr int kStages = 4;
 constexpr int kVRing = kStages * kTileBytes;  // LDS: K ring [0, 64 KiB), V ring [64 KiB, 128 KiB)
 constexpr int kPrefetch = 2;                  // tiles requested ahead of the one being computed
 constexpr int kPiecesPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB load instructions per tile per wave
-constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kPiecesPerWave == 2, "wait counts below assume 2 K + 2 V loads per wave per tile");
 static_assert(kBr == kMfmaRowsPerWg && kBc == kMfmaKeysPerTile, "host view of the work geometry");
 static_assert(kStages >= kPrefetch + 2, "a stage is reused only after both groups finished with it");
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-__device__ __forceinline__ float partner(float x) {
-  // value held by lane (lane ^ 32)
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const unsigned lane = __lane_id();
-  return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
-
-// s_waitcnt through the builtin, so the compiler's own wait bookkeeping sees it (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
 // all but this wave's most recent tile request (2 K + 2 V instructions) have landed in LDS
-__device__ __forceinline__ void wait_vmem_but_one_tile() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+__device__ __forceinline__ void wait_vmem_but_one_tile() { wait_vmem<4>(); }
 
 // Largest key index visible to the query at local row `row` (causal), clamped to [-1, nk-1].
 __device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int row, int nk) {
@@ -103,20 +83,6 @@ struct Ctx {
   uint32_t goff[kPiecesPerWave];  // byte offset of this lane's 16 B in each of its tile pieces
 };
 
-// One 16-byte global -> LDS copy per lane: lane l's bytes at gbase + voff land at LDS address
-// lds + 16 l.  Issued from inline assembly so that the compiler does not treat later LDS reads of
-// other stages as possibly overlapping the copy in flight (it would otherwise wait for every
-// outstanding global load before such reads).  The kernel tracks completion itself: vmcnt waits
-// and a workgroup barrier separate every copy from the first read of its stage.
-// The LDS address goes in M0 (bound through the operand constraint, so the compiler knows the
-// register's value); one wait state separates the M0 write from the load.
-__device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
-      "s"(gbase), "{m0}"(lds)
-      : "memory");
-}
 
 // This wave's share of one K/V tile request: 2 K + 2 V copies of 1 KiB (the wait counts rely on
 // exactly four).  The addresses are prepared ahead (make_request) so that the X phase only issues

@@ -78,6 +78,10 @@ extern "C" {
 /* ring_attn_step flags */
 #define RA_STEP_INIT 1 /* ignore the incoming state: treat it as m = -inf, l = 0, o_acc = 0 */
 
+/* ring_attn_bwd_step flags */
+#define RA_BWD_INIT_DQ 1  /* overwrite dq instead of adding to it */
+#define RA_BWD_INIT_DKV 2 /* overwrite dk and dv instead of adding to them */
+
 #define RA_MAX_DEV 64 /* largest ring size / number of devices batched into one call */
 #define RA_MAX_D 128  /* largest head dimension */
 
@@ -175,6 +179,72 @@ int ring_attn_plan(int P, int dev0, int n_local, int n, int mask, int layout, in
 /* Visible (query, key) pairs between query block i and key block j of a P-way ring with n tokens
  * per block under the given mask and layout (host arithmetic; -1 on invalid arguments). */
 int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j);
+
+/*
+ * Backward pass.  The pages use ring attention to train (Ultralytics "Ring Attention", section
+ * "Aplicações"; section "Como funciona a atenção em anel": striped attention raises training
+ * throughput) without writing the backward out; it is read here as the exact gradient of the same
+ * attention, run on the forward's ring schedule: device i keeps q_i, dO_i and the forward's lse_i and
+ * accumulates dq_i; the key/value block it holds carries its own dk, dv accumulators.  For one
+ * (query block, key/value block) pair, with x = log2(e) * scale * q.k:
+ *   p = 2^(x - lse2), lse2 = log2(e) * lse;  dp = dO . v;  ds = p * (dp - delta), delta = sum dO * O;
+ *   dq += scale * ds k;  dk += scale * ds^T q;  dv += p^T dO.
+ * Supported: bf16 with D == 128 (RA_ERR_UNSUPPORTED otherwise); gradients are fp32.
+ */
+
+/*
+ * ring_attn_bwd_prep — per-row quantities of the backward from the forward's results.
+ *   o, dout  [n_dev, B, Nq, Hq, D] (dtype)   forward output and its gradient
+ *   lse      [n_dev, B, Hq, Nq] fp32         forward log-sum-exp (natural log)
+ *   delta    [n_dev, B, Hq, Nq] fp32 out     sum_d dout * o
+ *   lse2     [n_dev, B, Hq, Nq] fp32 out     log2(e) * lse
+ * Any dtype and D <= RA_MAX_D.
+ */
+int ring_attn_bwd_prep(const void* o, const void* dout, const float* lse, float* delta, float* lse2, int n_dev,
+                       int B, int Hq, int Nq, int D, int dtype, void* stream);
+
+/*
+ * ring_attn_bwd_step — add the gradient contributions of n_dev independent (query block, key/value
+ * block) pairs: device t's queries q[t] against the block k[t], v[t], whose gradient accumulators
+ * are dk[t], dv[t] (they travel with the block; the caller moves them with it).
+ *   q, dout  [n_dev, B, Nq, Hq, D] bf16       lse2, delta [n_dev, B, Hq, Nq] fp32 (ring_attn_bwd_prep)
+ *   k, v     [n_dev, B, Nk, Hkv, D] bf16
+ *   dq       [n_dev, B, Nq, Hq, D] fp32       dk, dv [n_dev, B, Nk, Hkv, D] fp32  (in/out)
+ *   flags    RA_BWD_INIT_DQ | RA_BWD_INIT_DKV, or 0 to accumulate
+ * Positions, masking, scale and grouped-query heads as in ring_attn_step.  Fully masked pairs launch
+ * nothing (their outputs are only zeroed when an INIT flag asks for it).  Deterministic: each output
+ * row is written by one workgroup, without atomics.
+ */
+int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                       const float* delta, float* dq, float* dk, float* dv, int n_dev, int B, int Hq, int Hkv, int Nq,
+                       int Nk, int D, int dtype, float scale, int mask, const int64_t* q_off, int64_t q_stride,
+                       const int64_t* k_off, int64_t k_stride, int flags, void* stream);
+
+/*
+ * ring_attn_bwd_local — the backward ring for devices [dev0, dev0 + n_local) of a P-way ring
+ * (same schedule as ring_attn_local: in step s device i holds block (i - s) mod P).
+ *   q_local, o_local, dout_local [n_local, B, n, Hq, D] bf16    lse_local [n_local, B, Hq, n] fp32
+ *   k_src, v_src [P, B, n, Hkv, D] bf16, device memory
+ *   dq_local [n_local, B, n, Hq, D] fp32 out     gradient of the local devices' queries
+ *   dk, dv   [P, B, n, Hkv, D] fp32 out          gradient of every shard's keys and values from the
+ *                                                local devices' queries (the whole gradient when
+ *                                                n_local == P; otherwise this GPU's share, summed over
+ *                                                GPUs by the caller)
+ *   layout   RA_LAYOUT_CONTIGUOUS or RA_LAYOUT_STRIPED (zigzag: RA_ERR_UNSUPPORTED)
+ *   workspace >= ring_attn_bwd_local_workspace_bytes(...): two staging slots of K and V for the
+ *             local devices, and delta / lse2
+ * Blocks of steps s >= 1 are copied from their source shard into a staging slot on copy_stream,
+ * double-buffered against the kernels on compute_stream (step 0 reads the shards in place); each
+ * block's dk, dv accumulators are addressed where the block came from rather than copied along
+ * (same arithmetic, no traffic).  Both streams are left ordered after all of the call's work.
+ */
+int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_src, const void* o_local,
+                        const void* dout_local, const float* lse_local, float* dq_local, float* dk, float* dv, int P,
+                        int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype, float scale, int mask,
+                        int layout, void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream);
+
+/* Workspace size in bytes for ring_attn_bwd_local with these arguments (0 on invalid arguments). */
+size_t ring_attn_bwd_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype);
 
 /* Human-readable text for a status code (static storage). */
 const char* ring_attn_strerror(int code);

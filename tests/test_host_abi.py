@@ -183,3 +183,57 @@ def test_plan_rejects_bad_arguments():
     assert L.ring_attn_plan(4, 0, 4, 8, 0, 0, None) == -1
     assert L.ring_attn_visible_pairs(4, 8, 2, 0, 0, 0) == -1
     assert L.ring_attn_visible_pairs(4, 8, 1, 0, 4, 0) == -1
+
+
+# ---------------------------------------------------------------- backward entry points (validation)
+
+def _bwd_step(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, do=FAKE * 4, lse2=FAKE * 5, delta=FAKE * 6, dq=FAKE * 7, dk=FAKE * 8,
+             dv=FAKE * 9, n_dev=1, B=1, Hq=2, Hkv=1, Nq=4, Nk=4, D=128, dtype=1, scale=0.25, mask=0, q_off=None,
+             q_stride=1, k_off=None, k_stride=1, flags=0)
+    a.update(kw)
+    arr = lambda x: None if x is None else (ctypes.c_int64 * len(x))(*x)
+    return ra.lib().ring_attn_bwd_step(a["q"], a["k"], a["v"], a["do"], a["lse2"], a["delta"], a["dq"], a["dk"],
+                                       a["dv"], a["n_dev"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
+                                       a["dtype"], a["scale"], a["mask"], arr(a["q_off"]), a["q_stride"],
+                                       arr(a["k_off"]), a["k_stride"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(dk=None), -1), (dict(n_dev=0), -1), (dict(Hq=3, Hkv=2), -1), (dict(flags=4), -1),
+    (dict(scale=-1.0), -1), (dict(mask=1), -1), (dict(D=64), -2), (dict(dtype=0), -2), (dict(D=129), -2),
+    (dict(dq=FAKE), -1),            # dq aliases q
+    (dict(dv=FAKE * 8 + 64), -1),   # dv overlaps dk
+    (dict(Nq=0, Nk=0), 0),          # nothing to do
+])
+def test_bwd_step_rejects_bad_arguments(kw, code):
+    assert _bwd_step(**kw) == code
+
+
+def test_bwd_prep_and_local_reject_bad_arguments():
+    L = ra.lib()
+    p = L.ring_attn_bwd_prep
+    assert p(None, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 1, 2, 4, 16, 0, None) == -1
+    assert p(FAKE, FAKE * 2, FAKE * 3, FAKE, FAKE * 5, 1, 1, 2, 4, 16, 0, None) == -1      # delta aliases o
+    assert p(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 1, 2, 4, 200, 0, None) == -2
+    assert p(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 1, 2, 0, 16, 0, None) == 0   # empty
+    ws = ra.ring_attn_bwd_local_workspace_bytes(4, 4, 1, 2, 1, 8, 128, 1)
+    blk = 8 * 128 * 2
+    rows = 4 * 2 * 8
+    assert ws == 4 * ((4 * blk + 255) // 256 * 256) + 2 * ((rows * 4 + 255) // 256 * 256)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE * 8, v=FAKE * 16, o=FAKE * 24, do=FAKE * 32, lse=FAKE * 40, dq=FAKE * 48,
+                 dk=FAKE * 56, dv=FAKE * 64, P=4, dev0=0, n_local=4, B=1, Hq=2, Hkv=1, n=8, D=128, dtype=1,
+                 scale=0.25, mask=1, layout=0, ws=FAKE * 72, ws_bytes=ws)
+        a.update(kw)
+        return L.ring_attn_bwd_local(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                     a["P"], a["dev0"], a["n_local"], a["B"], a["Hq"], a["Hkv"], a["n"], a["D"],
+                                     a["dtype"], a["scale"], a["mask"], a["layout"], a["ws"], a["ws_bytes"], None, None)
+    assert call(ws_bytes=ws - 1) == -4
+    assert call(layout=2) == -2         # zigzag backward not provided
+    assert call(D=64) == -2 and call(dtype=0) == -2
+    assert call(layout=3) == -1 and call(dev0=4) == -1 and call(dk=None) == -1
+    assert call(dq=FAKE) == -1          # dq aliases q
+    assert call(ws=FAKE * 8) == -1      # workspace aliases k
+    assert call(n=0) == 0
