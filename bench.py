@@ -10,12 +10,13 @@ The default workload is the non-causal bf16 configuration the headline metric is
 (B=1, S=16384 as 8 shards of 2048, 8 heads, D=128, all 8 devices on the one GPU).  The causal
 workloads are reported under "extra" in the same JSON line: the striped grouped-query one (S=65536,
 32 query / 8 key-value heads), the same inputs under zigzag sharding, the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
-device's share of a 32-device ring over S=1048576 (8 heads); each runs about 1 s of warm-up and 2 s
-of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
+device's share of a 32-device ring over S=1048576 (8 heads), and the backward ring (gradients for a
+seeded output gradient, ``ring_attn_bwd_local``) of the non-causal 16k and the striped causal 64k
+workloads; each runs about 1 s of warm-up and 2 s of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
 fraction of the dense bf16 MFMA rate at that clock.
 
 FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
-runs count only the visible pairs.  Printed on stdout: one JSON line.  Progress goes to stderr.
+runs count only the visible pairs; the backward counts 10*D (five products of that size).  Printed on stdout: one JSON line.  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -165,6 +166,81 @@ def run_workload(w, steps, warmup, measure_clock=True):
     return res
 
 
+def run_backward_workload(w, measure_clock=True):
+    """The backward ring of workload ``w``: one forward call for O and LSE (untimed), then about 1 s of
+    warm-up and 2 s of timed ``ring_attn_bwd_local`` calls between HIP events on the compute stream."""
+    import numpy as np
+    import torch
+
+    import blockwise_ring_attention_step_amd as ra
+    import synth_inputs as si
+
+    t0 = time.time()
+    q, k, v = si.workload_qkv(w)
+    do = si.workload_dout(w)
+    n, dev0, n_local = w.n, 0, w.P
+
+    def up(x):
+        return torch.from_numpy(shard_np(x, w.P, w.layout).view(np.int16)).view(torch.bfloat16).cuda()
+
+    tq, tk, tv, tdo = up(q), up(k), up(v), up(do)
+    del q, k, v, do
+    o = torch.empty_like(tq)
+    lse = torch.empty((n_local, w.B, w.Hq, n), dtype=torch.float32, device="cuda")
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(w.D)
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(w.P, n_local, w.B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
+                     dtype=torch.uint8, device="cuda")
+    ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=w.causal, layout=w.layout,
+                       compute_stream=cs, copy_stream=xs)
+    del ws
+    dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+    wsb = torch.empty(ra.ring_attn_bwd_local_workspace_bytes(w.P, n_local, w.B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
+                      dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs generated, uploaded and forward run in {time.time() - t0:.1f}s")
+
+    def call():
+        ra.ring_attn_bwd_local(tq, tk, tv, o, tdo, lse, dq, dk, dv, wsb, P=w.P, dev0=dev0, scale=scale,
+                               causal=w.causal, layout=w.layout, compute_stream=cs, copy_stream=xs)
+
+    call()
+    torch.cuda.synchronize()
+    t1 = time.time()
+    call()
+    torch.cuda.synchronize()
+    one = max(time.time() - t1, 1e-4)
+    warmup = max(3, min(50, int(1.0 / one)))
+    steps = max(3, min(50, int(2.0 / one)))
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    bounds = [ra.HipEvent() for _ in range(steps + 1)]
+    bounds[0].record(cs)
+    for i in range(steps):
+        call()
+        bounds[i + 1].record(cs)
+    torch.cuda.synchronize()
+    ms = bounds[0].elapsed_ms(bounds[-1]) / steps
+    per_call = sorted(bounds[i].elapsed_ms(bounds[i + 1]) for i in range(steps))
+    pairs = sum(ra.ring_attn_visible_pairs(w.P, n, i, (i - s) % w.P, causal=w.causal, layout=w.layout)
+                for s in range(w.P) for i in range(w.P))
+    flops = 10.0 * w.D * w.Hq * w.B * pairs
+    assert abs(flops - w.flops()) <= 1e-6 * flops, (flops, w.flops())
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms:.3f} ms/call, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
+    if sclk:
+        log(f"{w.name}: GFX clock under this load {sclk:.0f} MHz (GPU busy for ~{100 * busy:.0f}% of the sampling)")
+    res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
+               ms_min=per_call[0], tflops=tflops, flops=flops, kernel_tflops=None, sclk_mhz=sclk, sclk_busy=busy)
+    del tq, tk, tv, tdo, o, lse, dq, dk, dv, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
 def sample_sclk(call, torch, ms_per_call, seconds=1.2):
     """(median GFX clock in MHz, GPU busy fraction) while the same calls keep the GPU busy: a
     background thread reads amdsmi every 10 ms while this thread keeps enqueuing calls for
@@ -276,7 +352,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
-    ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard",
+    ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
+                    "bwd_noncausal_16k,bwd_causal_striped_64k",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,14 +387,16 @@ def main():
     main_res = run_workload(w, args.steps, args.warmup, not args.no_clock)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
-        r = run_workload(si.WORKLOADS[name], None, None, not args.no_clock)
+        wx = si.WORKLOADS[name]
+        r = (run_backward_workload(wx, not args.no_clock) if wx.backward
+             else run_workload(wx, None, None, not args.no_clock))
         extras.append({"workload": name, "value": r["tflops"], "unit": "TFLOP/s", "steps": r["steps"],
                        "warmup": r["warmup"], "ms_per_step": r["ms"],
                        "ms_per_step_median": r["ms_median"], "ms_per_step_min": r["ms_min"],
                        "pct_of_peak": 100 * r["tflops"] / PEAK_BF16_TFLOPS, "step_kernel_tflops": r["kernel_tflops"],
                        "sclk_mhz": r["sclk_mhz"], "sclk_gpu_busy": r["sclk_busy"],
                        "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"]) if r["sclk_mhz"] else None),
-                       "causal": si.WORKLOADS[name].causal, "layout": si.WORKLOADS[name].layout})
+                       "causal": wx.causal, "layout": wx.layout, "pass": "backward" if wx.backward else "forward"})
 
     traffic = traffic_entry()
     roof = {"bound": "mfma", "kernel": "step_mfma_bf16_d128", "achieved": main_res["kernel_tflops"],

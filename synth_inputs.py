@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_bits", "bf16_to_f32", "normal_bf16", "normal_f32",
-    "demo_qkv", "workload_qkv",
+    "demo_qkv", "workload_qkv", "workload_dout",
 ]
 
 
@@ -43,6 +43,8 @@ class Workload:
     sigma: float = 1.0
     # for the one-device share: which shard is local (None = all shards emulated on one GPU)
     local_shard: int | None = None
+    # the backward ring (gradients for a seeded output gradient) instead of the forward
+    backward: bool = False
 
     @property
     def n(self) -> int:
@@ -58,8 +60,9 @@ class Workload:
         return i * n * n + n * (n + 1) // 2
 
     def flops(self) -> float:
-        """Algorithmic FLOPs: 2*D for Q.K^T plus 2*D for P.V per visible pair."""
-        return 4.0 * self.D * self.Hq * self.B * self.visible_pairs()
+        """Algorithmic FLOPs: 2*D for Q.K^T plus 2*D for P.V per visible pair; the backward counts
+        five such products (Q.K^T again, dO.V^T, P^T.dO, dS^T.Q, dS.K), 10*D per visible pair."""
+        return (10.0 if self.backward else 4.0) * self.D * self.Hq * self.B * self.visible_pairs()
 
 
 WORKLOADS = {
@@ -71,6 +74,10 @@ WORKLOADS = {
     "causal_zigzag_64k": Workload("causal_zigzag_64k", 1, 65536, 8, 32, 8, 128, True, "zigzag", "bf16", 4000),
     "causal_1m_shard": Workload("causal_1m_shard", 1, 1048576, 32, 8, 8, 128, True, "contiguous", "bf16", 5000,
                                 local_shard=31),
+    "bwd_noncausal_16k": Workload("bwd_noncausal_16k", 1, 16384, 8, 8, 8, 128, False, "contiguous", "bf16", 2000,
+                                  backward=True),
+    "bwd_causal_striped_64k": Workload("bwd_causal_striped_64k", 1, 65536, 8, 32, 8, 128, True, "striped", "bf16",
+                                       4000, backward=True),
 }
 
 
@@ -145,3 +152,10 @@ def workload_qkv(w: Workload):
     k = gen(w.seed + 1, (w.B, w.S, w.Hkv, w.D), w.sigma)
     v = gen(w.seed + 2, (w.B, w.S, w.Hkv, w.D), w.sigma)
     return q, k, v
+
+
+def workload_dout(w: Workload):
+    """Seeded output gradient dO for a backward workload, token order [B, S, Hq, D] (seed ``w.seed + 3``)."""
+    gen = normal_bf16 if w.dtype == "bf16" else normal_f32
+    sq = w.n if w.local_shard is not None else w.S
+    return gen(w.seed + 3, (w.B, sq, w.Hq, w.D), w.sigma)

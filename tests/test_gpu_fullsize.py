@@ -155,3 +155,68 @@ def test_striped_and_zigzag_match_contiguous_after_unpermuting():
         print(f"[fullsize] {layout} vs contiguous 64k: max|dO|={do:.3g} max|dLSE|={dl:.3g}", flush=True)
         assert math.isfinite(do) and math.isfinite(dl)
         assert do <= TOL_BF16_O and dl <= TOL_BF16_LSE
+
+
+def test_backward_noncausal_16k_sampled_rows_and_identities():
+    """The backward ring of the non-causal 16k workload at its full size: dQ on >= 4096 sampled rows
+    (plus every shard's first and last row) against the oracle, and dK, dV through identities that hold
+    at any size: each head's key gradients sum to zero (softmax rows are invariant to shifting every
+    key) and each key/value head's value gradients sum to the output gradients of its query heads
+    (softmax rows sum to one)."""
+    w = si.WORKLOADS["bwd_noncausal_16k"]
+    q, k, v = si.workload_qkv(w)
+    do = si.workload_dout(w)
+    pos = _shard_positions(w)
+    perm = pos.reshape(-1)
+    B, n, P = w.B, w.n, w.P
+
+    def up(x):
+        y = np.ascontiguousarray(x[:, perm].reshape(B, P, n, x.shape[2], w.D).transpose(1, 0, 2, 3, 4))
+        return torch.from_numpy(y.view(np.int16)).view(torch.bfloat16).cuda()
+
+    tq, tk, tv, tdo = up(q), up(k), up(v), up(do)
+    o = torch.empty_like(tq)
+    lse = torch.empty((P, B, w.Hq, n), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(w.D)
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(P, P, B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    xs = torch.cuda.Stream()
+    ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=P, dev0=0, scale=scale, causal=w.causal, layout=w.layout,
+                       copy_stream=xs)
+    dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
+    wsb = torch.empty(ra.ring_attn_bwd_local_workspace_bytes(P, P, B, w.Hq, w.Hkv, n, w.D, ra.RA_BF16),
+                      dtype=torch.uint8, device="cuda")
+    ra.ring_attn_bwd_local(tq, tk, tv, o, tdo, lse, dq, dk, dv, wsb, P=P, dev0=0, scale=scale, causal=w.causal,
+                           layout=w.layout, copy_stream=xs)
+    torch.cuda.synchronize()
+    # identities on every element of dK and dV (sums over the keys of each (batch, kv head), per d)
+    g = w.Hq // w.Hkv
+    dk64 = dk.double()
+    sum_k = dk64.sum(dim=(0, 2))                    # [B, Hkv, D]
+    abs_k = dk64.abs().sum(dim=(0, 2))
+    sum_v = dv.double().sum(dim=(0, 2))
+    do64 = torch.from_numpy(si.bf16_to_f32(do)).double().reshape(B, w.S, w.Hkv, g, w.D)
+    want_v = do64.sum(dim=(1, 3)).cuda()            # [B, Hkv, D]
+    ek = (sum_k.abs() / abs_k).max().item()
+    ev = ((sum_v - want_v).abs().max() / want_v.abs().max()).item()
+    print(f"[fullsize] backward 16k: |sum dK| / sum |dK| <= {ek:.3g}, sum dV vs sum dO rel {ev:.3g}", flush=True)
+    assert ek <= 1e-3 and ev <= 1e-3
+    # sampled rows of dQ against the oracle
+    rows = _sample_rows(w, 61, w.S)
+    shard_of = np.empty(w.S, dtype=np.int64)
+    local_of = np.empty(w.S, dtype=np.int64)
+    shard_of[perm] = np.repeat(np.arange(P), n)
+    local_of[perm] = np.tile(np.arange(n), P)
+    ti, tb, tr, th = (torch.from_numpy(x).cuda() for x in (shard_of[rows[:, 2]], rows[:, 0], local_of[rows[:, 2]],
+                                                              rows[:, 1]))
+    got = dq[ti, tb, tr, th].cpu().numpy().astype(np.float64)
+    del tq, tk, tv, tdo, o, lse, ws, dq, dk, dv, wsb
+    torch.cuda.empty_cache()
+    ref = oracle.attention_backward_rows(si.bf16_to_f32(q), si.bf16_to_f32(k), si.bf16_to_f32(v), si.bf16_to_f32(do),
+                                         rows, causal=w.causal)
+    emax = np.abs(got - ref).max() / np.abs(ref).max()
+    efro = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"[fullsize] backward 16k: dQ rows={len(rows)} max {emax:.3g} fro {efro:.3g} (relative)", flush=True)
+    assert emax <= 2e-2 and efro <= 1e-2
