@@ -12,12 +12,12 @@
 // where lse2 = log2(e) * lse and delta = sum_d dO * O of the row (the softmax Jacobian term).
 //
 // Two kernels, so that every output is owned by exactly one workgroup (no atomics, deterministic):
-//   bwd_dq:  query-stationary like the forward step: a workgroup holds 128 query rows (4 waves x 32),
+//   bwd_dq:  query-stationary like the forward step: a workgroup holds 256 query rows (8 waves x 32),
 //            streams 64-key tiles of K and V through LDS and computes, per 32-key half tile,
 //              S^T = K Q^T, dP^T = V dO^T (A = K / V rows from LDS, B = Q^T / dO^T in VGPRs),
 //              dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T (A = K^T by LDS transpose reads).
-//   bwd_dkv: key-stationary: a workgroup holds 128 keys (4 waves x 32, one wave per SIMD for the
-//            register budget), streams 64-row tiles of Q, dO, lse2 and delta of every query head
+//   bwd_dkv: key-stationary: a workgroup holds 128 keys (8 waves: each 32 keys belong to a value
+//            wave and a key wave), streams 64-row tiles of Q, dO, lse2 and delta of every query head
 //            that reads its key/value head, and computes, per 32-row chunk,
 //              S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = K^T / V^T in VGPRs),
 //              dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose reads).
@@ -26,6 +26,8 @@
 // chunk (bwd_dkv).  Tiles go HBM -> LDS directly (global_load_lds) through 3-stage rings in the
 // swizzled layout of gfx950_tile.h; tile t+2 is requested while tile t is computed and one
 // workgroup barrier per tile makes the next one visible.
+#include <type_traits>
+
 #include "gfx950_tile.h"
 #include "internal.h"
 
@@ -114,9 +116,8 @@ __device__ __forceinline__ bf16x8 pack_half(const float (&x)[16], int h) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// bwd_dq: 128 query rows per workgroup, 4 waves (one per SIMD: Q and dO fragments, the dQ
-// accumulator and two score-sized accumulators need more than the 256 registers of two waves).
-constexpr int kDqWaves = 4;
+// bwd_dq: 256 query rows per workgroup, 8 waves (two per SIMD).
+constexpr int kDqWaves = 8;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kDqVRing = kBwdStages * kTileBytes;  // LDS: K ring, then V ring
@@ -129,12 +130,11 @@ struct DqCtx {
   int wave;
 };
 
-__device__ __forceinline__ void dq_request(const DqCtx& cx, int t, const LDS_AS char* smem) {
+__device__ __forceinline__ void dq_request(const DqCtx& cx, int t, int stage, const LDS_AS char* smem) {
   TileSrc k = cx.k, v = cx.v;
   k.base += t * cx.tile_stride;
   v.base += t * cx.tile_stride;
   k.nrows = v.nrows = min(kTile, cx.nk - t * kTile);
-  const int stage = t % kBwdStages;
   const uint32_t kl = (uint32_t)(uintptr_t)(smem + stage * kTileBytes);
   load_tile_pieces(k, kl, cx.wave * kDqPieces, kDqPieces);
   load_tile_pieces(v, kl + kDqVRing, cx.wave * kDqPieces, kDqPieces);
@@ -208,38 +208,27 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   for (int dt = 0; dt < 4; ++dt) dqt[dt] = f32x16{};
 
   if (ntiles > 0) {
-    for (int t = 0; t < 2 && t < ntiles; ++t) dq_request(cx, t, smem);
+    for (int t = 0; t < 2 && t < ntiles; ++t) dq_request(cx, t, t, smem);
     wait_vmem<0>();
     __syncthreads();
   }
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) dq_request(cx, t + 2, smem);
+  // one key tile (t, LDS stage ST = t % 3); unrolled by three below so that every LDS address is a
+  // per-lane base plus an immediate
+  auto tile = [&](auto stage_tag, int t) {
+    constexpr int ST = decltype(stage_tag)::value;
+    if (t + 2 < ntiles) dq_request(cx, t + 2, (ST + 2) % kBwdStages, smem);
     const int key0 = t * kTile;
     if (key0 <= kmax_wave) {  // else no row of this wave sees the tile
-      const LDS_AS char* kt = smem + (t % kBwdStages) * kTileBytes;
+      const LDS_AS char* kt = smem + ST * kTileBytes;
       const LDS_AS char* vt = kt + kDqVRing;
       const bool masked = key0 + kTile - 1 > kmin_wave;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        // K and V rows are read two k steps ahead of their products (a ring of three), and the
-        // scheduling barriers keep the compiler from hoisting more reads (register budget)
         f32x16 s = {}, dp = {};
-        bf16x8 ka[3], va[3];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          ka[kk] = read_rows(kt, cc, to.rowoff[kk]);
-          va[kk] = read_rows(vt, cc, to.rowoff[kk]);
-        }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          if (kk + 2 < 8) {
-            ka[(kk + 2) % 3] = read_rows(kt, cc, to.rowoff[kk + 2]);
-            va[(kk + 2) % 3] = read_rows(vt, cc, to.rowoff[kk + 2]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          s = mfma(ka[kk % 3], qf[kk], s);
-          dp = mfma(va[kk % 3], df[kk], dp);
-          __builtin_amdgcn_sched_barrier(0);
+          s = mfma(read_rows(kt, cc, to.rowoff[kk]), qf[kk], s);
+          dp = mfma(read_rows(vt, cc, to.rowoff[kk]), df[kk], dp);
         }
         float ds[16];
 #pragma unroll
@@ -271,6 +260,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
         wait_vmem<0>();
       __syncthreads();
     }
+  };
+  for (int t = 0; t < ntiles; t += kBwdStages) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= ntiles) break;
+    tile(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 >= ntiles) break;
+    tile(std::integral_constant<int, 2>{}, t + 2);
   }
 
   // epilogue: dq (token-major, fp32) += scale * dQ; lane's row, d = 32 dt + 8 g + 4 h2 + i
@@ -292,12 +288,20 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 }
 
 // ------------------------------------------------------------------------------------------------
-// bwd_dkv: 128 keys per workgroup, 4 waves (one per SIMD).
-constexpr int kKvWaves = 4;
+// bwd_dkv: 128 keys per workgroup, 8 waves, two per SIMD.  Waves w and w + 4 share the keys
+// 32 (w % 4) .. + 31 and split the work, so that each holds one gradient accumulator and two waves
+// fit every SIMD.  Per query tile, in two halves separated by a workgroup barrier:
+//   value wave (w < 4): S = Q K^T, P = 2^(x - lse2) (kept as bf16, and stored to LDS in fp32) |
+//                       dV^T += dO^T P
+//   key wave (w >= 4):  dP = dO V^T                                                         |
+//                       dS = P (from LDS) * (dP - delta), dK^T += Q^T dS
+// Each wave issues 32 products per tile.
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvKeys = 32 * kKvWaves;
-constexpr int kKvStageBytes = 2 * kTileBytes + 1024;  // Q tile, dO tile, lse2 (256 B) + delta (256 B)
-constexpr int kKvPieces = 16 / kKvWaves;              // 1 KiB pieces per wave per Q (and per dO) tile
+constexpr int kKvKeys = 32 * (kKvWaves / 2);
+constexpr int kKvStageBytes = 2 * kTileBytes + 512;  // Q tile, dO tile, lse2 (256 B) + delta (256 B)
+constexpr int kKvPBytes = 4 * 2 * 64 * 64;           // P in fp32: 4 wave pairs x 2 halves x 64 lanes x 64 B
+constexpr int kKvPieces = 16 / kKvWaves;             // 1 KiB pieces per wave per Q (and per dO) tile
 
 struct KvCtx {
   const char* q;        // row 0 of the slot's query rows of query head 0 (batch bb), bytes
@@ -310,8 +314,8 @@ struct KvCtx {
   int wave;
 };
 
-// request tile `item` (query head hq, query tile qt) into its stage: 4 Q + 4 dO pieces, and 32 lanes
-// of lse2 or delta rows, 4 bytes each (waves 0, 1: lse2 rows 0-31, 32-63; waves 2, 3: delta rows)
+// request tile (query head hq, query tile qt) into a stage: 2 Q + 2 dO pieces per wave, and 16 lanes
+// of 4 bytes of lse2 (waves 0-3: rows 16 w .. + 15) or delta (waves 4-7)
 __device__ __forceinline__ void kv_request(const KvCtx& cx, int stage, int hq, int qt, const LDS_AS char* smem) {
   const uint32_t st = (uint32_t)(uintptr_t)(smem + stage * kKvStageBytes);
   const int nrows = min(kTile, cx.nq - qt * kTile);
@@ -319,19 +323,22 @@ __device__ __forceinline__ void kv_request(const KvCtx& cx, int stage, int hq, i
   load_tile_pieces(TileSrc{cx.q + rowsel, cx.row_bytes, nrows}, st, cx.wave * kKvPieces, kKvPieces);
   load_tile_pieces(TileSrc{cx.dout + rowsel, cx.row_bytes, nrows}, st + kTileBytes, cx.wave * kKvPieces, kKvPieces);
   const int lane = __lane_id();
-  if (lane < 32) {
-    const char* src = (cx.wave < 2 ? cx.lse2 : cx.delta) + hq * cx.head_stat;
-    const int row = qt * kTile + (cx.wave & 1) * 32 + lane;
+  if (lane < 16) {
+    const char* src = (cx.wave < 4 ? cx.lse2 : cx.delta) + hq * cx.head_stat;
+    const int row = qt * kTile + (cx.wave & 3) * 16 + lane;
     const int srow = row < cx.nq ? row : cx.nq - 1;  // rows past the end re-read the last (masked)
-    copy_to_lds4(src, (uint32_t)(srow * 4), st + 2 * kTileBytes + (cx.wave >> 1) * 256 + (cx.wave & 1) * 128);
+    copy_to_lds4(src, (uint32_t)(srow * 4), st + 2 * kTileBytes + (cx.wave >> 2) * 256 + (cx.wave & 3) * 64);
   }
 }
 
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kBwdStages * kKvStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kBwdStages * kKvStageBytes + kKvPBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool key_wave = wave >= kKvWaves / 2;  // accumulates dK (else dV)
+  // this pair's P buffer: [half][group g][lane] f32x4 (registers 4 g .. 4 g + 3 of the lane)
+  LDS_AS f32x4* pbuf = (LDS_AS f32x4*)(smem + kBwdStages * kKvStageBytes) + (wave & 3) * 2 * 4 * 64;
   const int j = lane & 31, h2 = lane >> 5;
 
   // work item: (slot, batch, key/value head, key tile of 128)
@@ -345,8 +352,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   const int gsz = p.Hq / p.Hkv;
   const int qdev = p.qslot[dl], kvdev = p.kvslot[dl], gdev = p.gslot[dl];
   const int Nq = p.Nq, nk = p.nk[dl], row0 = p.q_row0[dl];
-  const int key = ktile * kKvKeys + wave * 32 + j;  // this lane's key
   if (ktile * kKvKeys >= nk) return;
+  const int key = ktile * kKvKeys + (wave & 3) * 32 + j;  // this lane's key
   const bool kvalid = key < nk;
 
   // causal: first query row that sees this lane's key, of the wave's keys and of the workgroup's
@@ -359,21 +366,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   };
   const int klast = min(ktile * kKvKeys + kKvKeys, nk) - 1;
   const int qmin_lane = first_row(kvalid ? key : klast);
-  const int wk0 = min(ktile * kKvKeys + wave * 32, klast), wk1 = min(ktile * kKvKeys + wave * 32 + 31, klast);
+  const int wk0 = min(ktile * kKvKeys + (wave & 3) * 32, klast), wk1 = min(ktile * kKvKeys + (wave & 3) * 32 + 31, klast);
   const int qmin_wave = first_row(wk0), qmax_wave = first_row(wk1);  // rows >= qmax_wave see every key of the wave
   const int qt_first = first_row(ktile * kKvKeys) / kTile;
   const int nqt = (Nq + kTile - 1) / kTile;
   const int nitems = (nqt - qt_first) * gsz;  // (query head, query tile) pairs, head-major
 
-  // this lane's key: K^T and V^T fragments (B operands)
+  // this lane's key: K^T fragments (B operand of S, value wave) or V^T fragments (of dP, key wave)
   const size_t krow_elems = (size_t)p.Hkv * kD;
   const size_t kbase = (((size_t)kvdev * p.B + bb) * p.NkTot + (kvalid ? key : 0)) * krow_elems + (size_t)kvh * kD;
-  bf16x8 kf[8], vf[8];
+  const unsigned short* frag_src = (const unsigned short*)(key_wave ? p.v : p.k) + kbase;
+  bf16x8 kvf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const i16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    kf[kk] = __builtin_bit_cast(bf16x8, kvalid ? *(const i16x8*)((const unsigned short*)p.k + kbase + 16 * kk + 8 * h2) : z);
-    vf[kk] = __builtin_bit_cast(bf16x8, kvalid ? *(const i16x8*)((const unsigned short*)p.v + kbase + 16 * kk + 8 * h2) : z);
+    kvf[kk] = __builtin_bit_cast(bf16x8, kvalid ? *(const i16x8*)(frag_src + 16 * kk + 8 * h2) : z);
   }
 
   KvCtx cx;
@@ -390,9 +397,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   const TileOffsets to = tile_offsets();
   const float c = p.scale_log2;
 
-  f32x16 dkt[4], dvt[4];
+  f32x16 acc[4];  // dK^T (key wave) or dV^T (value wave): lane's key, d = 32 dt + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) dkt[dt] = dvt[dt] = f32x16{};
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
   auto item_tile = [&](int it, int& hq, int& qt) {
     hq = it / (nqt - qt_first);
@@ -408,58 +415,97 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
     __syncthreads();
   }
   constexpr int kPerRequest = 2 * kKvPieces + 1;  // vector-memory instructions per wave per request
-  for (int it = 0; it < nitems; ++it) {
+  // one query tile (item it, LDS stage ST = it % 3); unrolled by three below so that every LDS
+  // address is a per-lane base plus an immediate
+  auto tile = [&](auto stage_tag, int it) {
+    constexpr int ST = decltype(stage_tag)::value;
     if (it + 2 < nitems) {
       int hq2, qt2;
       item_tile(it + 2, hq2, qt2);
-      kv_request(cx, (it + 2) % kBwdStages, hq2, qt2, smem);
+      kv_request(cx, (ST + 2) % kBwdStages, hq2, qt2, smem);
     }
     int hq, qt;
     item_tile(it, hq, qt);
     const int q0 = qt * kTile;
-    if (q0 + kTile > qmin_wave) {  // else no key of this wave is seen by the tile's rows
-      const LDS_AS char* st = smem + (it % kBwdStages) * kKvStageBytes;
-      const LDS_AS char* qtl = st;
-      const LDS_AS char* dtl = st + kTileBytes;
-      const LDS_AS float* lsel = (const LDS_AS float*)(st + 2 * kTileBytes);
-      const LDS_AS float* dell = lsel + kTile;
-      const bool masked = q0 < qmax_wave || q0 + kTile > Nq;
+    const bool work = q0 + kTile > qmin_wave;  // else no key of this wave (pair) is seen by the tile's rows
+    const LDS_AS char* st = smem + ST * kKvStageBytes;
+    const LDS_AS char* qtl = st;
+    const LDS_AS char* dtl = st + kTileBytes;
+    const LDS_AS float* lsel = (const LDS_AS float*)(st + 2 * kTileBytes);
+    const LDS_AS float* dell = lsel + kTile;
+    const bool masked = q0 < qmax_wave || q0 + kTile > Nq;
+    // first half: P (value wave) or dP (key wave) of the two 32-row halves, in the same registers
+    f32x16 t2[2];
+    if (work) {
+      if (!key_wave) {
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        f32x16 s = {}, dp = {};
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x16 sc = {};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          s = mfma(read_rows(qtl, c2, to.rowoff[kk]), kf[kk], s);
-          dp = mfma(read_rows(dtl, c2, to.rowoff[kk]), vf[kk], dp);
-        }
-        // row of register r: 32 c2 + 8 (r / 4) + 4 h2 + r % 4
-        float pr[16], ds[16];
+          for (int kk = 0; kk < 8; ++kk) sc = mfma(read_rows(qtl, c2, to.rowoff[kk]), kvf[kk], sc);
+          // row of register r: 32 c2 + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rbase = 32 * c2 + 8 * g + 4 * h2;
-          const f32x4 l4 = *(const LDS_AS f32x4*)(lsel + rbase);
-          const f32x4 d4 = *(const LDS_AS f32x4*)(dell + rbase);
+          for (int g = 0; g < 4; ++g) {
+            const int rbase = 32 * c2 + 8 * g + 4 * h2;
+            const f32x4 l4 = *(const LDS_AS f32x4*)(lsel + rbase);
+            f32x4 p4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            const float l2 = l4[i] == -INFINITY ? INFINITY : l4[i];
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
-            if (masked) {
-              const int row = q0 + rbase + i;
-              if (row < qmin_lane || row >= Nq) x = 0.f;
+            for (int i = 0; i < 4; ++i) {
+              const float l2 = l4[i] == -INFINITY ? INFINITY : l4[i];
+              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g + i], c, -l2));
+              if (masked) {
+                const int row = q0 + rbase + i;
+                if (row < qmin_lane || row >= Nq) pr = 0.f;
+              }
+              t2[c2][4 * g + i] = pr;
+              p4[i] = pr;
             }
-            pr[r] = x;
-            ds[r] = x * (dp[r] - d4[i]);
+            pbuf[(c2 * 4 + g) * 64 + lane] = p4;
           }
         }
+      } else {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 bp = pack_half(pr, hh);
-          const bf16x8 bs = pack_half(ds, hh);
+        for (int c2 = 0; c2 < 2; ++c2) {
+          t2[c2] = f32x16{};
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            dvt[dt] = mfma(read_transposed(dtl, 2 * c2 + hh, to, dt), bp, dvt[dt]);
-            dkt[dt] = mfma(read_transposed(qtl, 2 * c2 + hh, to, dt), bs, dkt[dt]);
+          for (int kk = 0; kk < 8; ++kk) t2[c2] = mfma(read_rows(dtl, c2, to.rowoff[kk]), kvf[kk], t2[c2]);
+        }
+      }
+    }
+    __syncthreads();  // P of this tile is in LDS
+    // second half: dV^T += dO^T P (value wave) or dS = P (dP - delta), dK^T += Q^T dS (key wave)
+    if (work) {
+      if (!key_wave) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          float x[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = t2[c2][r];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8 b = pack_half(x, hh);
+            __builtin_amdgcn_sched_barrier(0);  // bounds how far the scheduler hoists operand reads
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(read_transposed(dtl, 2 * c2 + hh, to, dt), b, acc[dt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          float x[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 p4 = pbuf[(c2 * 4 + g) * 64 + lane];
+            const f32x4 d4 = *(const LDS_AS f32x4*)(dell + 32 * c2 + 8 * g + 4 * h2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * g + i] = p4[i] * (t2[c2][4 * g + i] - d4[i]);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8 b = pack_half(x, hh);
+            __builtin_amdgcn_sched_barrier(0);  // bounds how far the scheduler hoists operand reads
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(read_transposed(qtl, 2 * c2 + hh, to, dt), b, acc[dt]);
           }
         }
       }
@@ -471,33 +517,32 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
         wait_vmem<0>();
       __syncthreads();
     }
+  };
+  for (int it = 0; it < nitems; it += kBwdStages) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 >= nitems) break;
+    tile(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 >= nitems) break;
+    tile(std::integral_constant<int, 2>{}, it + 2);
   }
 
-  // epilogue: dk += scale * dK, dv += dV (token-major, fp32); lane's key, d = 32 dt + 8 g + 4 h2 + i
+  // epilogue: dk += scale * dK or dv += dV (token-major, fp32); lane's key, d = 32 dt + 8 g + 4 h2 + i
   if (!kvalid) return;
   const size_t grow = (((size_t)gdev * p.B + bb) * p.NkTot + key) * krow_elems + (size_t)kvh * kD;
-  float* dkrow = p.dk + grow;
-  float* dvrow = p.dv + grow;
+  float* row = (key_wave ? p.dk : p.dv) + grow;
+  const float mul = key_wave ? p.scale : 1.f;
   const bool init = p.flags[dl] & kBwdInitDkv;
-  f32x4 ok[16], ov[16];
+  f32x4 old[16];
 #pragma unroll
-  for (int cI = 0; cI < 16; ++cI) {
-    const int off = 32 * (cI >> 2) + 8 * (cI & 3) + 4 * h2;
-    ok[cI] = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(dkrow + off);
-    ov[cI] = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(dvrow + off);
-  }
+  for (int cI = 0; cI < 16; ++cI)
+    old[cI] = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(row + 32 * (cI >> 2) + 8 * (cI & 3) + 4 * h2);
 #pragma unroll
   for (int cI = 0; cI < 16; ++cI) {
     const int dt = cI >> 2, g = cI & 3;
-    const int off = 32 * dt + 8 * g + 4 * h2;
-    f32x4 nk4, nv4;
+    f32x4 nv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      nk4[i] = ok[cI][i] + p.scale * dkt[dt][4 * g + i];
-      nv4[i] = ov[cI][i] + dvt[dt][4 * g + i];
-    }
-    *(f32x4*)(dkrow + off) = nk4;
-    *(f32x4*)(dvrow + off) = nv4;
+    for (int i = 0; i < 4; ++i) nv[i] = old[cI][i] + mul * acc[dt][4 * g + i];
+    *(f32x4*)(row + 32 * dt + 8 * g + 4 * h2) = nv;
   }
 }
 
