@@ -188,8 +188,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
     df[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const i16x8*)((const unsigned short*)p.dout + qbase + 16 * kk + 8 * h2) : zq);
   }
   const size_t srow = (((size_t)qdev * p.B + bb) * p.Hq + h) * p.NqTot + row0 + (qvalid ? qr : 0);
-  float lse2 = qvalid ? p.lse2[srow] : INFINITY;
-  if (lse2 == -INFINITY) lse2 = INFINITY;  // a row that saw no key has p = 0 everywhere
+  const float lse2 = qvalid ? p.lse2[srow] : INFINITY;  // +inf for a row that saw no key: p = 0
   const float delta = qvalid ? p.delta[srow] : 0.f;
   const float c = p.scale_log2;
 
@@ -230,16 +229,18 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
           s = mfma(read_rows(kt, cc, to.rowoff[kk]), qf[kk], s);
           dp = mfma(read_rows(vt, cc, to.rowoff[kk]), df[kk], dp);
         }
-        float ds[16];
+        float pr[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-          if (masked) {
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        if (masked) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * cc + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (key > kmax_lane) pr = 0.f;
+            if (key > kmax_lane) pr[r] = 0.f;
           }
-          ds[r] = pr * (dp[r] - delta);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dp[r] - delta);
         const bf16x8 b0 = pack_half(ds, 0), b1 = pack_half(ds, 1);
         bf16x8 ta[3];
         ta[0] = read_transposed(kt, 2 * cc, to, 0);
@@ -401,15 +402,19 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  auto item_tile = [&](int it, int& hq, int& qt) {
-    hq = it / (nqt - qt_first);
-    qt = qt_first + it % (nqt - qt_first);
+  // items walk (query head, query tile) head-major: the query tile of the current item, and the
+  // item requested next
+  int qt = qt_first, rhq = 0, rqt = qt_first;
+  auto advance = [&](int& h_, int& q_) {
+    if (++q_ == nqt) {
+      q_ = qt_first;
+      ++h_;
+    }
   };
   if (nitems > 0) {
     for (int it = 0; it < 2 && it < nitems; ++it) {
-      int hq, qt;
-      item_tile(it, hq, qt);
-      kv_request(cx, it, hq, qt, smem);
+      kv_request(cx, it, rhq, rqt, smem);
+      advance(rhq, rqt);
     }
     wait_vmem<0>();
     __syncthreads();
@@ -420,13 +425,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   auto tile = [&](auto stage_tag, int it) {
     constexpr int ST = decltype(stage_tag)::value;
     if (it + 2 < nitems) {
-      int hq2, qt2;
-      item_tile(it + 2, hq2, qt2);
-      kv_request(cx, (ST + 2) % kBwdStages, hq2, qt2, smem);
+      kv_request(cx, (ST + 2) % kBwdStages, rhq, rqt, smem);
+      advance(rhq, rqt);
     }
-    int hq, qt;
-    item_tile(it, hq, qt);
     const int q0 = qt * kTile;
+    qt = qt + 1 == nqt ? qt_first : qt + 1;
     const bool work = q0 + kTile > qmin_wave;  // else no key of this wave (pair) is seen by the tile's rows
     const LDS_AS char* st = smem + ST * kKvStageBytes;
     const LDS_AS char* qtl = st;
@@ -444,24 +447,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) sc = mfma(read_rows(qtl, c2, to.rowoff[kk]), kvf[kk], sc);
           // row of register r: 32 c2 + 8 (r / 4) + 4 h2 + r % 4
+          f32x4 l4[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int rbase = 32 * c2 + 8 * g + 4 * h2;
-            const f32x4 l4 = *(const LDS_AS f32x4*)(lsel + rbase);
-            f32x4 p4;
+          for (int g = 0; g < 4; ++g) l4[g] = *(const LDS_AS f32x4*)(lsel + 32 * c2 + 8 * g + 4 * h2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float l2 = l4[i] == -INFINITY ? INFINITY : l4[i];
-              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g + i], c, -l2));
-              if (masked) {
-                const int row = q0 + rbase + i;
-                if (row < qmin_lane || row >= Nq) pr = 0.f;
-              }
-              t2[c2][4 * g + i] = pr;
-              p4[i] = pr;
+          for (int r = 0; r < 16; ++r) t2[c2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l4[r >> 2][r & 3]));
+          if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = q0 + 32 * c2 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+              if (row < qmin_lane || row >= Nq) t2[c2][r] = 0.f;
             }
-            pbuf[(c2 * 4 + g) * 64 + lane] = p4;
           }
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            pbuf[(c2 * 4 + g) * 64 + lane] = f32x4{t2[c2][4 * g], t2[c2][4 * g + 1], t2[c2][4 * g + 2], t2[c2][4 * g + 3]};
         }
       } else {
 #pragma unroll
@@ -547,7 +547,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
 }
 
 // ------------------------------------------------------------------------------------------------
-// delta = sum_d dout * out and lse2 = log2(e) * lse per (device, batch, head, row); 16 lanes per row.
+// delta = sum_d dout * out and lse2 = log2(e) * lse (+inf where lse = -inf) per (device, batch, head,
+// row); 16 lanes per row.
 template <bool BF16>
 __device__ __forceinline__ float load_val(const void* p, size_t i) {
   if constexpr (BF16)
@@ -575,7 +576,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
   for (int w = 8; w >= 1; w /= 2) acc += __shfl_xor(acc, w, 16);
   if (sub == 0) {
     delta[r] = acc;
-    lse2[r] = lse[r] * kLog2e;
+    const float l = lse[r];
+    lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;  // a row that saw no key gets p = 2^(x - inf) = 0
   }
 }
 
