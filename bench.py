@@ -39,7 +39,9 @@ CUS, BF16_FLOP_PER_CLK_PER_CU = 256, 4096  # dense bf16 MFMA rate per CU per clo
 def clock_peak(sclk_mhz):
     """Dense bf16 MFMA peak (TFLOP/s) at the measured GFX clock."""
     return CUS * BF16_FLOP_PER_CLK_PER_CU * sclk_mhz * 1e6 / 1e12
-KERNEL_SOURCE = os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", "step_mfma_bf16.hip")
+# the sources the forward step kernel is compiled from (its HBM traffic summary is tied to them)
+KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", f)
+                  for f in ("step_mfma_bf16.hip", "gfx950_tile.h", "internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
 EVENT_EVERY = 4  # timed calls between two that carry per-step kernel events
 
@@ -49,8 +51,11 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def shard_np(x, P, layout):
