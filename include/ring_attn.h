@@ -197,7 +197,8 @@ int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j
  *   o, dout  [n_dev, B, Nq, Hq, D] (dtype)   forward output and its gradient
  *   lse      [n_dev, B, Hq, Nq] fp32         forward log-sum-exp (natural log)
  *   delta    [n_dev, B, Hq, Nq] fp32 out     sum_d dout * o
- *   lse2     [n_dev, B, Hq, Nq] fp32 out     log2(e) * lse
+ *   lse2     [n_dev, B, Hq, Nq] fp32 out     log2(e) * lse, and +inf where lse = -inf (a row that
+ *                                            sees no key: its p is then 2^(x - inf) = 0)
  * Any dtype and D <= RA_MAX_D.
  */
 int ring_attn_bwd_prep(const void* o, const void* dout, const float* lse, float* delta, float* lse2, int n_dev,
