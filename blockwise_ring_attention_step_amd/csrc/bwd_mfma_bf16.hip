@@ -147,16 +147,20 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 31, h2 = lane >> 5;
 
-  // work item: (slot, batch, query head, query tile); causal: heaviest query tiles first
-  int w = blockIdx.x;
-  const int qt_rank = w % p.n_qtiles;
-  w /= p.n_qtiles;
-  const int h = w % p.Hq;
-  w /= p.Hq;
-  const int bb = w % p.B;
-  const int dl = w / p.B;
+  // work item: the workgroups that read one (slot, batch, key/value head)'s keys and values (all its
+  // query heads and query tiles) run on one XCD (blockIdx mod 8), so they share its L2; causal:
+  // heaviest query tiles first
+  const int gsz = p.Hq / p.Hkv;
+  const int per_group = gsz * p.n_qtiles;
+  const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+  const int gi = sl / per_group, rem = sl - gi * per_group;
+  const int grp = gi * 8 + xcd;
+  if (grp >= p.groups) return;
+  const int qt_rank = rem / gsz, hq = rem - qt_rank * gsz;
+  const int kvh = grp % p.Hkv, bt = grp / p.Hkv;
+  const int dl = bt / p.B, bb = bt - dl * p.B;
+  const int h = kvh * gsz + hq;
   const int qt = p.causal ? p.n_qtiles - 1 - qt_rank : qt_rank;
-  const int gsz = p.Hq / p.Hkv, kvh = h / gsz;
   const int qdev = p.qslot[dl], kvdev = p.kvslot[dl];
   const int Nq = p.Nq, nk = p.nk[dl], row0 = p.q_row0[dl];
   const int qr = qt * kDqRows + wave * 32 + j;  // this lane's query row within the slot
@@ -342,14 +346,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   LDS_AS f32x4* pbuf = (LDS_AS f32x4*)(smem + kBwdStages * kKvStageBytes) + (wave & 3) * 2 * 4 * 64;
   const int j = lane & 31, h2 = lane >> 5;
 
-  // work item: (slot, batch, key/value head, key tile of 128)
-  int w = blockIdx.x;
-  const int ktile = w % p.n_ktiles;
-  w /= p.n_ktiles;
-  const int kvh = w % p.Hkv;
-  w /= p.Hkv;
-  const int bb = w % p.B;
-  const int dl = w / p.B;
+  // work item: (slot, batch, key/value head, key tile of 128); the key tiles of one (slot, batch,
+  // key/value head) read the same query rows and run on one XCD (blockIdx mod 8), sharing its L2
+  const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+  const int gi = sl / p.n_ktiles, ktile = sl - gi * p.n_ktiles;
+  const int grp = gi * 8 + xcd;
+  if (grp >= p.groups) return;
+  const int kvh = grp % p.Hkv, bt = grp / p.Hkv;
+  const int dl = bt / p.B, bb = bt - dl * p.B;
   const int gsz = p.Hq / p.Hkv;
   const int qdev = p.qslot[dl], kvdev = p.kvslot[dl], gdev = p.gslot[dl];
   const int Nq = p.Nq, nk = p.nk[dl], row0 = p.q_row0[dl];
@@ -597,7 +601,9 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream) {
 hipError_t launch_bwd_dq_bf16_d128(const BwdParams& p_in, hipStream_t stream) {
   BwdParams p = p_in;
   p.n_qtiles = (p.Nq + kDqRows - 1) / kDqRows;
-  const long long grid = (long long)p.n_launch * p.B * p.Hq * p.n_qtiles;
+  p.groups = p.n_launch * p.B * p.Hkv;
+  p.groups_per_xcd = (p.groups + 7) / 8;
+  const long long grid = 8LL * p.groups_per_xcd * (p.Hq / p.Hkv) * p.n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dq_bf16_d128, dim3((unsigned)grid), dim3(kDqThreads), 0, stream, p);
@@ -607,7 +613,9 @@ hipError_t launch_bwd_dq_bf16_d128(const BwdParams& p_in, hipStream_t stream) {
 hipError_t launch_bwd_dkv_bf16_d128(const BwdParams& p_in, hipStream_t stream) {
   BwdParams p = p_in;
   p.n_ktiles = (p.Nk + kKvKeys - 1) / kKvKeys;
-  const long long grid = (long long)p.n_launch * p.B * p.Hkv * p.n_ktiles;
+  p.groups = p.n_launch * p.B * p.Hkv;
+  p.groups_per_xcd = (p.groups + 7) / 8;
+  const long long grid = 8LL * p.groups_per_xcd * p.n_ktiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dkv_bf16_d128, dim3((unsigned)grid), dim3(kKvThreads), 0, stream, p);
