@@ -11,8 +11,8 @@ The default workload is the non-causal bf16 configuration the headline metric is
 workloads are reported under "extra" in the same JSON line: the striped grouped-query one (S=65536,
 32 query / 8 key-value heads), the same inputs under zigzag sharding, the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
 device's share of a 32-device ring over S=1048576 (8 heads), and the backward ring (gradients for a
-seeded output gradient, ``ring_attn_bwd_local``) of the non-causal 16k and the striped causal 64k
-workloads; each runs about 1 s of warm-up and 2 s of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
+seeded output gradient, ``ring_attn_bwd_local``) of the non-causal 16k and the striped and zigzag causal
+64k workloads; each runs about 1 s of warm-up and 2 s of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
 fraction of the dense bf16 MFMA rate at that clock.
 
 FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
@@ -358,7 +358,7 @@ def main():
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
     ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
-                    "bwd_noncausal_16k,bwd_causal_striped_64k",
+                    "bwd_noncausal_16k,bwd_causal_striped_64k,bwd_causal_zigzag_64k",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

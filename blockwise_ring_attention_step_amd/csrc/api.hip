@@ -710,7 +710,8 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
   if (!valid_layout(layout)) return RA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
-  if (!uses_mfma_kernel(dtype, D) || layout == RA_LAYOUT_ZIGZAG) return RA_ERR_UNSUPPORTED;
+  if (!uses_mfma_kernel(dtype, D)) return RA_ERR_UNSUPPORTED;
+  if (layout == RA_LAYOUT_ZIGZAG && n % 2) return RA_ERR_INVALID_ARG;
   if (n == 0) return RA_OK;
   if (!q_local || !k_src || !v_src || !o_local || !dout_local || !lse_local || !dq_local || !dk || !dv || !workspace)
     return RA_ERR_INVALID_ARG;
@@ -748,27 +749,32 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   const bool causal = mask == RA_MASK_CAUSAL;
   const int64_t st = layout_stride(layout, P);
 
-  // schedule: class of every (step, device); first computed step of each device's query gradient
-  // and first visit of each block's key/value gradient
-  std::vector<int> cls((size_t)P * n_local);
-  std::vector<int> dq_first(n_local, -1), dkv_first(P, -1);
-  std::vector<uint8_t> first_flags((size_t)P * n_local, 0);
+  // schedule over units (a device's whole query block, or one of its two zigzag chunks, as in the
+  // forward): class of every (step, unit), the first computed step of each unit's query gradient and
+  // the first visit of each block's key/value gradient.  Zigzag units of one device read overlapping
+  // key rows of the same block, so their key/value gradients start from zero and always accumulate.
+  const int nh = layout == RA_LAYOUT_ZIGZAG ? 2 : 1;
+  const int n_units = n_local * nh;
+  std::vector<int> cls((size_t)P * n_units);
+  std::vector<int> dq_first(n_units, -1), dkv_first(P, -1);
+  std::vector<uint8_t> first_flags((size_t)P * n_units, 0);
   for (int s = 0; s < P; ++s)
-    for (int t = 0; t < n_local; ++t) {
-      const int i = dev0 + t, j = ((i - s) % P + P) % P;
-      const int c = classify(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n);
-      cls[(size_t)s * n_local + t] = c;
+    for (int u = 0; u < n_units; ++u) {
+      const int i = dev0 + u / nh, j = ((i - s) % P + P) % P;
+      const Unit un = ring_unit(causal, layout, P, n, i, j, u % nh);
+      const int c = classify(causal, un.q_off, un.stride, n / nh, un.k_off, un.stride, un.nk);
+      cls[(size_t)s * n_units + u] = c;
       if (c == 0) continue;
       uint8_t f = 0;
-      if (dq_first[t] < 0) {
-        dq_first[t] = s;
+      if (dq_first[u] < 0) {
+        dq_first[u] = s;
         f |= ra::kBwdInitDq;
       }
       if (dkv_first[j] < 0) {
         dkv_first[j] = s;
-        f |= ra::kBwdInitDkv;
+        if (nh == 1) f |= ra::kBwdInitDkv;
       }
-      first_flags[(size_t)s * n_local + t] = f;
+      first_flags[(size_t)s * n_units + u] = f;
     }
 
   hipEvent_t ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr}, ev_fork = nullptr;
@@ -818,6 +824,10 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   };
 
   RA_CHECK(ra::launch_bwd_prep(o_local, dout_local, lse_local, delta, lse2, n_local, B, Hq, n, D, dtype, cs));
+  if (nh == 2) {
+    RA_CHECK(ra::launch_zero_f32(dk, dkv_bytes / 4, cs));
+    RA_CHECK(ra::launch_zero_f32(dv, dkv_bytes / 4, cs));
+  }
   for (int s = 0; s < P; ++s) {
     if (s + 1 < P) {  // copies for step s+1, into the slot that step s-1 read
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
@@ -838,37 +848,57 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
-    p.Nq = p.NqTot = n;
-    p.Nk = p.NkTot = n;
+    p.Nq = n / nh;
+    p.NqTot = n;
+    p.NkTot = n;
     p.D = D;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     p.scale_log2 = (float)(scale * kLog2e);
-    p.q_stride = st;
-    p.k_stride = st;
-    for (int t = 0; t < n_local; ++t) {
-      if (cls[(size_t)s * n_local + t] == 0) continue;
-      const int i = dev0 + t, j = ((i - s) % P + P) % P;
-      const int x = p.n_launch++;
-      p.qslot[x] = p.kvslot[x] = t;
-      p.gslot[x] = j;
-      p.q_row0[x] = 0;
-      p.nk[x] = n;
-      p.q_off[x] = block_offset(layout, P, n, i);
-      p.k_off[x] = block_offset(layout, P, n, j);
-      p.flags[x] = first_flags[(size_t)s * n_local + t];
-    }
-    if (p.n_launch > 0) {
-      RA_CHECK(ra::launch_bwd_dq_bf16_d128(p, cs));
-      RA_CHECK(ra::launch_bwd_dkv_bf16_d128(p, cs));
+    // launches of step s: the query gradients of every unit (RA_MAX_DEV slots per launch), then the
+    // key/value gradients, one launch per zigzag half (the two halves of a device touch the same rows)
+    auto launch_units = [&](int half_sel, bool dq_pass) -> hipError_t {
+      std::vector<int> todo;
+      for (int u = 0; u < n_units; ++u)
+        if (cls[(size_t)s * n_units + u] != 0 && (half_sel < 0 || u % nh == half_sel)) todo.push_back(u);
+      for (size_t a0 = 0; a0 < todo.size(); a0 += RA_MAX_DEV) {
+        p.n_launch = 0;
+        p.Nk = 0;
+        for (size_t a = a0; a < todo.size() && a < a0 + RA_MAX_DEV; ++a) {
+          const int u = todo[a], t = u / nh;
+          const int i = dev0 + t, j = ((i - s) % P + P) % P;
+          const Unit un = ring_unit(causal, layout, P, n, i, j, u % nh);
+          const int x = p.n_launch++;
+          p.qslot[x] = p.kvslot[x] = t;
+          p.gslot[x] = j;
+          p.q_row0[x] = un.row0;
+          p.nk[x] = un.nk;
+          p.Nk = std::max(p.Nk, un.nk);
+          p.q_off[x] = un.q_off;
+          p.k_off[x] = un.k_off;
+          p.q_stride = un.stride;  // the same for every unit of a layout
+          p.k_stride = un.stride;
+          p.flags[x] = first_flags[(size_t)s * n_units + u];
+        }
+        const hipError_t e = dq_pass ? ra::launch_bwd_dq_bf16_d128(p, cs) : ra::launch_bwd_dkv_bf16_d128(p, cs);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    };
+    RA_CHECK(launch_units(-1, true));
+    if (nh == 1) {
+      RA_CHECK(launch_units(-1, false));
+    } else {
+      RA_CHECK(launch_units(0, false));
+      RA_CHECK(launch_units(1, false));
     }
     if (s + 2 < P) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
-  // gradients nothing contributed to: zero
+  // gradients nothing contributed to: zero (a zigzag unit always sees its own block's keys)
   const size_t qn = (size_t)B * n * Hq * D, kn = (size_t)B * n * Hkv * D;
-  for (int t = 0; t < n_local; ++t)
+  for (int t = 0; t < n_local && nh == 1; ++t)
     if (dq_first[t] < 0) RA_CHECK(ra::launch_zero_f32(dq_local + t * qn, qn, cs));
-  for (int j = 0; j < P; ++j)
+  for (int j = 0; j < P && nh == 1; ++j)
     if (dkv_first[j] < 0) {
       RA_CHECK(ra::launch_zero_f32(dk + j * kn, kn, cs));
       RA_CHECK(ra::launch_zero_f32(dv + j * kn, kn, cs));

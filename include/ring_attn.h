@@ -231,7 +231,8 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
  *                                                local devices' queries (the whole gradient when
  *                                                n_local == P; otherwise this GPU's share, summed over
  *                                                GPUs by the caller)
- *   layout   RA_LAYOUT_CONTIGUOUS or RA_LAYOUT_STRIPED (zigzag: RA_ERR_UNSUPPORTED)
+ *   layout   RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED or RA_LAYOUT_ZIGZAG (n even; the two chunks of a
+ *            device run as two units, as in ring_attn_local)
  *   workspace >= ring_attn_bwd_local_workspace_bytes(...): two staging slots of K and V for the
  *             local devices, and delta / lse2
  * Blocks of steps s >= 1 are copied from their source shard into a staging slot on copy_stream,

@@ -78,6 +78,8 @@ WORKLOADS = {
                                   backward=True),
     "bwd_causal_striped_64k": Workload("bwd_causal_striped_64k", 1, 65536, 8, 32, 8, 128, True, "striped", "bf16",
                                        4000, backward=True),
+    "bwd_causal_zigzag_64k": Workload("bwd_causal_zigzag_64k", 1, 65536, 8, 32, 8, 128, True, "zigzag", "bf16",
+                                      4000, backward=True),
 }
 
 

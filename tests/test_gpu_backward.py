@@ -111,9 +111,16 @@ def test_bwd_ring_small(gpu_lib, causal, layout, n):
     _check(2, 4, n, 4, 2, causal, layout, 900 + n)
 
 
+@pytest.mark.parametrize("causal,n", [(True, 128), (True, 200), (False, 96)])
+def test_bwd_zigzag_ring(gpu_lib, causal, n):
+    """Zigzag shards: each device's two chunks are separate units (ragged chunks of 64, 100, 48 rows)."""
+    _check(2, 4, n, 4, 2, causal, "zigzag", 990 + n)
+
+
 def test_bwd_ring_gqa_p8_and_partly_local(gpu_lib):
     _check(1, 8, 96, 8, 2, True, "striped", 950)
     _check(1, 6, 160, 4, 2, True, "contiguous", 960, dev0=2, n_local=3)
+    _check(1, 6, 160, 4, 2, True, "zigzag", 970, dev0=2, n_local=3)
 
 
 def test_bwd_step_accumulates_and_splits(gpu_lib):

@@ -231,7 +231,7 @@ def test_bwd_prep_and_local_reject_bad_arguments():
                                      a["P"], a["dev0"], a["n_local"], a["B"], a["Hq"], a["Hkv"], a["n"], a["D"],
                                      a["dtype"], a["scale"], a["mask"], a["layout"], a["ws"], a["ws_bytes"], None, None)
     assert call(ws_bytes=ws - 1) == -4
-    assert call(layout=2) == -2         # zigzag backward not provided
+    assert call(layout=2, n=7) == -1    # zigzag needs n even
     assert call(D=64) == -2 and call(dtype=0) == -2
     assert call(layout=3) == -1 and call(dev0=4) == -1 and call(dk=None) == -1
     assert call(dq=FAKE) == -1          # dq aliases q
