@@ -16,8 +16,8 @@ What is here, in float64 NumPy:
 * :func:`attention_backward_reference`, :func:`attention_backward_rows` — the gradients dQ, dK, dV
   of the same definition for an output gradient dO (chain rule written out; the pages use the ring
   for training but do not spell out its backward pass).
-* :func:`ffn_reference`, :func:`gelu` — the position-wise feed-forward that the blockwise method
-  computes after attention, y = gelu(x W1 + b1) W2 + b2.
+* :func:`ffn_reference`, :func:`gelu`, :func:`relu` — the position-wise feed-forward that the blockwise
+  method computes after attention, y = act(x W1 + b1) W2 + b2.
 * :mod:`oracle.layout` — contiguous, striped and zigzag token-to-shard assignment.
 
 Every function is pinned by CPU tests to facts outside itself (the pages' demonstration, library
@@ -25,11 +25,11 @@ routines, closed forms, brute force); none is "parity unpinned".
 """
 from .attention import attention_reference, attention_rows, ring_replay
 from .backward import attention_backward_reference, attention_backward_rows
-from .ffn import ffn_reference, gelu
+from .ffn import ffn_reference, gelu, relu
 from .layout import shard_positions, striped_permutation, contiguous_permutation, zigzag_permutation
 
 __all__ = [
     "attention_reference", "attention_rows", "ring_replay",
-    "attention_backward_reference", "attention_backward_rows", "ffn_reference", "gelu",
+    "attention_backward_reference", "attention_backward_rows", "ffn_reference", "gelu", "relu",
     "shard_positions", "striped_permutation", "contiguous_permutation", "zigzag_permutation",
 ]

@@ -6,9 +6,10 @@ attention and the feed-forward block by block, with the key/value exchange hidde
 The pages give no formula for the feed-forward.  Reading taken (the plainest that fits): the
 transformer's position-wise feed-forward applied to each token's attention output,
 
-    y = gelu(x W1 + b1) W2 + b2,     gelu(z) = z * Phi(z) = z * (1 + erf(z / sqrt(2))) / 2,
+    y = act(x W1 + b1) W2 + b2,
 
-computed over blocks of tokens, so that only one block's hidden activations [block, d_ff] exist at
+with act the exact gelu(z) = z * Phi(z) = z * (1 + erf(z / sqrt(2))) / 2 (Phi the standard normal
+CDF) or, as an option, the original transformer's max(z, 0), computed over blocks of tokens, so that only one block's hidden activations [block, d_ff] exist at
 a time.  Being position-wise, the result does not depend on the block size; the oracle is the
 formula itself, evaluated on all tokens at once.
 """
@@ -17,7 +18,7 @@ from __future__ import annotations
 import numpy as np
 from scipy.special import erf
 
-__all__ = ["gelu", "ffn_reference"]
+__all__ = ["gelu", "relu", "ffn_reference"]
 
 
 def gelu(z):
@@ -26,13 +27,19 @@ def gelu(z):
     return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
 
 
-def ffn_reference(x, w1, b1, w2, b2):
-    """y [N, d_model] = gelu(x W1 + b1) W2 + b2 in float64.
+def relu(z):
+    """max(z, 0), float64."""
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+def ffn_reference(x, w1, b1, w2, b2, activation="gelu"):
+    """y [N, d_model] = act(x W1 + b1) W2 + b2 in float64, act = gelu or relu.
 
     x [N, d_model], w1 [d_model, d_ff], b1 [d_ff], w2 [d_ff, d_model], b2 [d_model].
     """
+    act = {"gelu": gelu, "relu": relu}[activation]
     x, w1, b1, w2, b2 = (np.asarray(a, dtype=np.float64) for a in (x, w1, b1, w2, b2))
     if x.ndim != 2 or w1.shape != (x.shape[1], b1.shape[0]) or w2.shape != (b1.shape[0], x.shape[1]) \
             or b2.shape != (x.shape[1],):
         raise ValueError("shapes: x [N, dm], w1 [dm, dff], b1 [dff], w2 [dff, dm], b2 [dm]")
-    return gelu(x @ w1 + b1) @ w2 + b2
+    return act(x @ w1 + b1) @ w2 + b2

@@ -3,7 +3,7 @@
 gelu against values of the normal CDF (Phi(1) = 0.8413447460685429..., Phi(-1) = 1 - Phi(1)), its
 limits and odd-part identity gelu(z) - gelu(-z) = z; the whole feed-forward against torch's exact
 gelu and float64 matmuls (library routines); closed forms (zero first weights give the same row for
-every token; zero second weights give the bias); and position-wise structure (permuting tokens
+every token; zero second weights give the bias; gelu and relu agree far from zero); and position-wise structure (permuting tokens
 permutes the output, so any blocking of the tokens gives the same result).
 """
 import numpy as np
@@ -27,13 +27,23 @@ def test_gelu_values():
     assert abs(oracle.gelu(40.0) - 40.0) < 1e-12 and abs(oracle.gelu(-40.0)) < 1e-12
 
 
+@pytest.mark.parametrize("activation", ["gelu", "relu"])
 @pytest.mark.parametrize("N,dm,dff", [(5, 8, 16), (37, 32, 64)])
-def test_ffn_matches_torch(N, dm, dff):
+def test_ffn_matches_torch(N, dm, dff, activation):
     x, w1, b1, w2, b2 = _rand((N, dm), 1), _rand((dm, dff), 2, 0.2), _rand(dff, 3), _rand((dff, dm), 4, 0.2), _rand(dm, 5)
-    y = oracle.ffn_reference(x, w1, b1, w2, b2)
+    y = oracle.ffn_reference(x, w1, b1, w2, b2, activation=activation)
     t = lambda a: torch.tensor(a, dtype=torch.float64)
-    ref = torch.nn.functional.gelu(t(x) @ t(w1) + t(b1), approximate="none") @ t(w2) + t(b2)
+    h = t(x) @ t(w1) + t(b1)
+    h = torch.nn.functional.gelu(h, approximate="none") if activation == "gelu" else torch.relu(h)
+    ref = h @ t(w2) + t(b2)
     assert np.abs(y - ref.numpy()).max() < 1e-12
+
+
+def test_relu_and_gelu_agree_far_from_zero():
+    # Phi(z) -> 1 for large z and z Phi(z) -> 0 for very negative z: both activations coincide there
+    z = np.concatenate([np.linspace(-40, -12, 20), np.linspace(12, 40, 20)])
+    assert np.abs(oracle.gelu(z) - oracle.relu(z)).max() < 1e-12
+    assert np.all(oracle.relu(-np.abs(z)) == 0) and np.all(oracle.relu(np.abs(z)) == np.abs(z))
 
 
 def test_ffn_closed_forms_and_position_wise():
