@@ -8,15 +8,15 @@ transformer's position-wise feed-forward applied to each token's attention outpu
 
     y = act(x W1 + b1) W2 + b2,
 
-with act the exact gelu(z) = z * Phi(z) = z * (1 + erf(z / sqrt(2))) / 2 (Phi the standard normal
-CDF) or, as an option, the original transformer's max(z, 0), computed over blocks of tokens, so that only one block's hidden activations [block, d_ff] exist at
+with act the exact gelu(z) = z * Phi(z) (Phi the standard normal CDF, Phi(z) = erfc(-z / sqrt 2) / 2:
+the erfc form keeps Phi's relative precision in the lower tail, where 1 + erf(z / sqrt 2) cancels) or, as an option, the original transformer's max(z, 0), computed over blocks of tokens, so that only one block's hidden activations [block, d_ff] exist at
 a time.  Being position-wise, the result does not depend on the block size; the oracle is the
 formula itself, evaluated on all tokens at once.
 """
 from __future__ import annotations
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 __all__ = ["gelu", "relu", "ffn_reference"]
 
@@ -24,7 +24,7 @@ __all__ = ["gelu", "relu", "ffn_reference"]
 def gelu(z):
     """z * Phi(z) with the exact normal CDF, float64."""
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+    return 0.5 * z * erfc(-z / np.sqrt(2.0))
 
 
 def relu(z):

@@ -1,6 +1,7 @@
 """Pins of the feed-forward oracle to facts outside itself (no GPU needed).
 
-gelu against values of the normal CDF (Phi(1) = 0.8413447460685429..., Phi(-1) = 1 - Phi(1)), its
+gelu against values of the normal CDF (Phi(1) = 0.8413447460685429..., Phi(-1) = 1 - Phi(1), and
+the lower tail Phi(-5), Phi(-10) to relative precision), its
 limits and odd-part identity gelu(z) - gelu(-z) = z; the whole feed-forward against torch's exact
 gelu and float64 matmuls (library routines); closed forms (zero first weights give the same row for
 every token; zero second weights give the bias; gelu and relu agree far from zero); and position-wise structure (permuting tokens
@@ -25,6 +26,9 @@ def test_gelu_values():
     z = np.linspace(-6, 6, 101)
     assert np.abs(oracle.gelu(z) - oracle.gelu(-z) - z).max() < 1e-13  # z Phi(z) + z Phi(-z) = z
     assert abs(oracle.gelu(40.0) - 40.0) < 1e-12 and abs(oracle.gelu(-40.0)) < 1e-12
+    # the lower tail keeps its relative precision: Phi(-10) = 7.619853024160527e-24, Phi(-5) = 2.866515718791939e-07
+    assert abs(oracle.gelu(-10.0) / (-10.0 * 7.619853024160527e-24) - 1) < 1e-12
+    assert abs(oracle.gelu(-5.0) / (-5.0 * 2.866515718791939e-07) - 1) < 1e-12
 
 
 @pytest.mark.parametrize("activation", ["gelu", "relu"])
