@@ -10,5 +10,6 @@ from ._binding import (  # noqa: F401
     RA_MAX_D, RA_MAX_DEV, RA_STEP_INIT, RA_BWD_INIT_DQ, RA_BWD_INIT_DKV, RingAttnError, HipEvent, lib, lib_path, ring_attn_finalize, ring_attn_local,
     ring_attn_local_workspace_bytes, ring_attn_plan, ring_attn_step, ring_attn_strerror, ring_attn_visible_pairs,
     ring_attn_bwd_prep, ring_attn_bwd_step, ring_attn_bwd_local, ring_attn_bwd_local_workspace_bytes,
+    RA_FFN_GELU, RA_FFN_RELU, ring_attn_ffn, ring_attn_ffn_workspace_bytes,
     EXPORTED_SYMBOLS,
 )

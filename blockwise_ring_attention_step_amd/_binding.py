@@ -27,11 +27,14 @@ def _layout_code(layout, striped):
 RA_STEP_INIT = 1
 RA_BWD_INIT_DQ, RA_BWD_INIT_DKV = 1, 2
 RA_MAX_DEV, RA_MAX_D = 64, 128
+RA_FFN_GELU, RA_FFN_RELU = 0, 1
+_ACTIVATIONS = {"gelu": RA_FFN_GELU, "relu": RA_FFN_RELU}
 
 EXPORTED_SYMBOLS = (
     "ring_attn_step", "ring_attn_finalize", "ring_attn_local", "ring_attn_local_workspace_bytes",
     "ring_attn_plan", "ring_attn_visible_pairs", "ring_attn_strerror",
     "ring_attn_bwd_prep", "ring_attn_bwd_step", "ring_attn_bwd_local", "ring_attn_bwd_local_workspace_bytes",
+    "ring_attn_ffn", "ring_attn_ffn_workspace_bytes",
 )
 
 _lib = None
@@ -81,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_bwd_local.restype = i32
     L.ring_attn_bwd_local_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     L.ring_attn_bwd_local_workspace_bytes.restype = sz
+    L.ring_attn_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp, sz, vp]
+    L.ring_attn_ffn.restype = i32
+    L.ring_attn_ffn_workspace_bytes.argtypes = [i64, i32, i32, i64]
+    L.ring_attn_ffn_workspace_bytes.restype = sz
     L.ring_attn_strerror.argtypes = [i32]
     L.ring_attn_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -248,6 +255,32 @@ def ring_attn_bwd_local(q_local, k_src, v_src, o_local, dout_local, lse_local, d
                                    _layout_code(layout, striped), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), cs, xs)
     _check("ring_attn_bwd_local", rc)
+
+
+def ring_attn_ffn_workspace_bytes(n_tokens, d_model, d_ff, block_tokens):
+    return int(lib().ring_attn_ffn_workspace_bytes(int(n_tokens), int(d_model), int(d_ff), int(block_tokens)))
+
+
+def ring_attn_ffn(x, w1, b1, w2, b2, y, workspace, *, block_tokens, activation="gelu", stream=None):
+    """y = act(x w1^T + b1) w2^T + b2 over the tokens (rows) of x, one block of block_tokens at a time.
+
+    x, y [..., d_model] bf16 (y may be x); w1 [d_ff, d_model], b1 [d_ff], w2 [d_model, d_ff], b2 [d_model] bf16;
+    workspace: a device buffer of at least ring_attn_ffn_workspace_bytes(...) bytes."""
+    d_ff, d_model = w1.shape
+    if x.shape[-1] != d_model or y.shape != x.shape or tuple(w2.shape) != (d_model, d_ff):
+        raise ValueError("shapes: x, y [..., d_model], w1 [d_ff, d_model], w2 [d_model, d_ff]")
+    if tuple(b1.shape) != (d_ff,) or tuple(b2.shape) != (d_model,):
+        raise ValueError("shapes: b1 [d_ff], b2 [d_model]")
+    for t in (x, w1, b1, w2, b2, y):
+        if _dtype_code(t) != RA_BF16:
+            raise ValueError("ring_attn_ffn takes bf16 tensors")
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"unknown activation {activation!r}")
+    n_tokens = x.numel() // d_model
+    rc = lib().ring_attn_ffn(_ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y), n_tokens, d_model, d_ff,
+                             int(block_tokens), _ACTIVATIONS[activation], _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ring_attn_ffn", rc)
 
 
 _HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000

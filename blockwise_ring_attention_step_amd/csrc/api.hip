@@ -914,4 +914,60 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   return RA_OK;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Blockwise feed-forward after attention.
+
+size_t ring_attn_ffn_workspace_bytes(int64_t n_tokens, int d_model, int d_ff, int64_t block_tokens) {
+  if (n_tokens < 0 || block_tokens < 1) return 0;
+  if (d_model < 64 || d_model > 65536 || d_model % 64 || d_ff < 64 || d_ff > 65536 || d_ff % 64) return 0;
+  const int64_t rows = std::max<int64_t>(1, std::min(n_tokens, block_tokens));  // one block's tokens
+  if (rows > INT32_MAX) return 0;
+  return (size_t)rows * d_ff * 2;
+}
+
+int ring_attn_ffn(const void* x, const void* w1, const void* b1, const void* w2, const void* b2, void* y,
+                  int64_t n_tokens, int d_model, int d_ff, int64_t block_tokens, int activation, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  const size_t need = ring_attn_ffn_workspace_bytes(n_tokens, d_model, d_ff, block_tokens);
+  if (need == 0) return RA_ERR_INVALID_ARG;
+  if (activation != RA_FFN_GELU && activation != RA_FFN_RELU) return RA_ERR_INVALID_ARG;
+  if (mul_sizes({n_tokens, d_model, 2}) < 0) return RA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return RA_OK;
+  if (!x || !w1 || !b1 || !w2 || !b2 || !y || !workspace) return RA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return RA_ERR_WORKSPACE;
+  const size_t act_bytes = (size_t)n_tokens * d_model * 2;
+  const size_t w_bytes = (size_t)d_ff * d_model * 2;
+  const void* ins[5] = {x, w1, b1, w2, b2};
+  const size_t in_sz[5] = {act_bytes, w_bytes, (size_t)d_ff * 2, w_bytes, (size_t)d_model * 2};
+  for (int a = 0; a < 5; ++a) {
+    if (overlaps(workspace, need, ins[a], in_sz[a])) return RA_ERR_INVALID_ARG;
+    if (a > 0 && overlaps(y, act_bytes, ins[a], in_sz[a])) return RA_ERR_INVALID_ARG;
+  }
+  if (y != x && overlaps(y, act_bytes, x, act_bytes)) return RA_ERR_INVALID_ARG;
+  if (overlaps(y, act_bytes, workspace, need)) return RA_ERR_INVALID_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  for (int64_t t0 = 0; t0 < n_tokens; t0 += block_tokens) {
+    const int M = (int)std::min(block_tokens, n_tokens - t0);
+    ra::FfnGemmParams up{};
+    up.x = (const char*)x + t0 * d_model * 2;
+    up.w = w1;
+    up.bias = b1;
+    up.out = workspace;
+    up.M = M, up.N = d_ff, up.K = d_model;
+    up.ldx = d_model, up.ldw = d_model, up.ldo = d_ff;
+    hipError_t e = ra::launch_ffn_gemm_bf16(up, activation, st);
+    if (e != hipSuccess) return RA_ERR_HIP;
+    ra::FfnGemmParams down{};
+    down.x = workspace;
+    down.w = w2;
+    down.bias = b2;
+    down.out = (char*)y + t0 * d_model * 2;
+    down.M = M, down.N = d_model, down.K = d_ff;
+    down.ldx = d_ff, down.ldw = d_ff, down.ldo = d_model;
+    e = ra::launch_ffn_gemm_bf16(down, ra::kFfnActNone, st);
+    if (e != hipSuccess) return RA_ERR_HIP;
+  }
+  return RA_OK;
+}
+
 }  // extern "C"

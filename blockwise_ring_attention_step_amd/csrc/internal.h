@@ -89,6 +89,19 @@ struct BwdParams {
   uint8_t flags[RA_MAX_DEV];
 };
 
+// One projection of the blockwise feed-forward: out[m, n] = act(sum_k x[m, k] w[n, k] + bias[n]) in
+// bf16, fp32 accumulation.  Rows are strided (elements); K and N are multiples of 64.
+struct FfnGemmParams {
+  const void* x;     // [M, K] bf16, row stride ldx
+  const void* w;     // [N, K] bf16, row stride ldw
+  const void* bias;  // [N] bf16
+  void* out;         // [M, N] bf16, row stride ldo
+  int M, N, K;
+  int64_t ldx, ldw, ldo;
+  int tiles_m, tiles_n;  // filled in by the launcher
+};
+constexpr int kFfnActNone = -1;  // activation code of the second projection (bias only)
+
 // Work geometry of the bf16 D=128 step kernel that the host also needs (the in-step hop): query rows
 // per workgroup and keys per tile.
 constexpr int kMfmaRowsPerWg = 256;
@@ -105,6 +118,8 @@ hipError_t launch_bwd_dkv_bf16_d128(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2, int n_dev,
                            int B, int Hq, int Nq, int D, int dtype, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
+// act: RA_FFN_GELU, RA_FFN_RELU or kFfnActNone
+hipError_t launch_ffn_gemm_bf16(const FfnGemmParams& p, int act, hipStream_t stream);
 hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
                            int B, int Hq, int Nq, int D, int out_dtype, hipStream_t stream);
 hipError_t launch_init_state(float* o_acc, float* m, float* l, int n_dev_total, const int* slots, int n_slots,

@@ -82,6 +82,10 @@ extern "C" {
 #define RA_BWD_INIT_DQ 1  /* overwrite dq instead of adding to it */
 #define RA_BWD_INIT_DKV 2 /* overwrite dk and dv instead of adding to them */
 
+/* ring_attn_ffn activations */
+#define RA_FFN_GELU 0 /* exact gelu: z * Phi(z), Phi the standard normal CDF */
+#define RA_FFN_RELU 1 /* max(z, 0) */
+
 #define RA_MAX_DEV 64 /* largest ring size / number of devices batched into one call */
 #define RA_MAX_D 128  /* largest head dimension */
 
@@ -247,6 +251,32 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
 
 /* Workspace size in bytes for ring_attn_bwd_local with these arguments (0 on invalid arguments). */
 size_t ring_attn_bwd_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype);
+
+/*
+ * ring_attn_ffn — the position-wise feed-forward that follows attention, computed one block of
+ * tokens at a time.  The context-parallelism article on cyberairomania.ro (section on Ring
+ * Attention) has the method compute attention and the feed-forward block by block; the pages give no
+ * formula, and the one used is the transformer's feed-forward of each token's attention output:
+ *   y = act(x W1^T + b1) W2^T + b2
+ *   x      [n_tokens, d_model] bf16     tokens as rows, e.g. ring_attn_local's output viewed as
+ *                                       [n_local * B * n, Hq * D]
+ *   w1     [d_ff, d_model] bf16         b1 [d_ff] bf16     (weights as nn.Linear stores them:
+ *   w2     [d_model, d_ff] bf16         b2 [d_model] bf16   one row per output feature)
+ *   y      [n_tokens, d_model] bf16 out  may be x itself (in place); no other overlap
+ *   block_tokens  tokens per block (>= 1): one block's hidden activations act(x W1^T + b1),
+ *                 [min(block_tokens, n_tokens), d_ff] bf16, live in the workspace
+ *   activation    RA_FFN_GELU or RA_FFN_RELU
+ *   workspace     device memory, >= ring_attn_ffn_workspace_bytes(...)
+ * d_model and d_ff are multiples of 64 in [64, 65536].  Products accumulate in fp32; the hidden
+ * activations are rounded to bf16 before the second product, the output when stored.  Per block,
+ * two kernels on `stream` (bias, activation and rounding fused into their epilogues).
+ */
+int ring_attn_ffn(const void* x, const void* w1, const void* b1, const void* w2, const void* b2, void* y,
+                  int64_t n_tokens, int d_model, int d_ff, int64_t block_tokens, int activation, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Workspace size in bytes for ring_attn_ffn with these arguments (0 on invalid arguments). */
+size_t ring_attn_ffn_workspace_bytes(int64_t n_tokens, int d_model, int d_ff, int64_t block_tokens);
 
 /* Human-readable text for a status code (static storage). */
 const char* ring_attn_strerror(int code);

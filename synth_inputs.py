@@ -14,6 +14,14 @@ Workload recipes (token-major layout ``[B, S, H, D]``, as a sequence of tokens e
 * ``causal_striped_64k``: B=1, S=65536, 32 query heads, 8 KV heads, D=128, P=8, N(0,1), bf16.
 * ``causal_1m_shard``: one device's share of a 1,048,576-token ring of 32 shards (n=32768):
   local queries = the last shard, K/V = the whole sequence, 8 heads, D=128, N(0,1), bf16.
+
+Feed-forward workloads (the blockwise feed-forward after attention; the pages give no sizes, so
+d_model = Hq * D of an attention workload and d_ff = 4 d_model): x ~ N(0, 1) (an attention output
+has O(1) entries), w1 ~ N(0, 1/d_model), w2 ~ N(0, 1/d_ff) (variance-preserving initialisation, so
+the hidden and output activations are O(1) too), b1, b2 ~ N(0, 0.1^2), all rounded to bf16.
+
+* ``ffn_16k``: the 16384 tokens of ``noncausal_16k``'s output, d_model 1024, d_ff 4096.
+* ``ffn_32h_4k``: 4096 tokens of the 32-head configurations, d_model 4096, d_ff 16384.
 """
 from __future__ import annotations
 
@@ -23,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_bits", "bf16_to_f32", "normal_bf16", "normal_f32",
-    "demo_qkv", "workload_qkv", "workload_dout",
+    "demo_qkv", "workload_qkv", "workload_dout", "FfnWorkload", "FFN_WORKLOADS", "ffn_inputs",
 ]
 
 
@@ -161,3 +169,35 @@ def workload_dout(w: Workload):
     gen = normal_bf16 if w.dtype == "bf16" else normal_f32
     sq = w.n if w.local_shard is not None else w.S
     return gen(w.seed + 3, (w.B, sq, w.Hq, w.D), w.sigma)
+
+
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    name: str
+    tokens: int
+    d_model: int
+    d_ff: int
+    block_tokens: int
+    activation: str  # "gelu" or "relu"
+    seed: int
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of the two projections: 2 * d_model * d_ff per token each."""
+        return 4.0 * self.tokens * self.d_model * self.d_ff
+
+
+FFN_WORKLOADS = {
+    "ffn_16k": FfnWorkload("ffn_16k", 16384, 1024, 4096, 16384, "gelu", 6000),
+    "ffn_32h_4k": FfnWorkload("ffn_32h_4k", 4096, 4096, 16384, 4096, "gelu", 6100),
+}
+
+
+def ffn_inputs(seed: int, tokens: int, d_model: int, d_ff: int):
+    """x [tokens, d_model], w1 [d_ff, d_model], b1 [d_ff], w2 [d_model, d_ff], b2 [d_model] as bf16 bit
+    patterns (seeds seed + 0..4; weights in nn.Linear layout, one row per output feature)."""
+    x = normal_bf16(seed, (tokens, d_model))
+    w1 = normal_bf16(seed + 1, (d_ff, d_model), 1.0 / np.sqrt(d_model))
+    b1 = normal_bf16(seed + 2, (d_ff,), 0.1)
+    w2 = normal_bf16(seed + 3, (d_model, d_ff), 1.0 / np.sqrt(d_ff))
+    b2 = normal_bf16(seed + 4, (d_model,), 0.1)
+    return x, w1, b1, w2, b2

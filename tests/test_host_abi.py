@@ -237,3 +237,30 @@ def test_bwd_prep_and_local_reject_bad_arguments():
     assert call(dq=FAKE) == -1          # dq aliases q
     assert call(ws=FAKE * 8) == -1      # workspace aliases k
     assert call(n=0) == 0
+
+
+def test_ffn_workspace_and_rejects_bad_arguments():
+    L = ra.lib()
+    assert ra.ring_attn_ffn_workspace_bytes(1000, 128, 512, 256) == 256 * 512 * 2
+    assert ra.ring_attn_ffn_workspace_bytes(100, 128, 512, 256) == 100 * 512 * 2   # one block of all tokens
+    assert ra.ring_attn_ffn_workspace_bytes(0, 128, 512, 256) == 512 * 2
+    for bad in ((10, 96, 512, 4), (10, 128, 500, 4), (10, 128, 512, 0), (-1, 128, 512, 4), (10, 0, 512, 4),
+                (10, 128, 65600, 4), (1 << 40, 128, 64, 1 << 40)):
+        assert ra.ring_attn_ffn_workspace_bytes(*bad) == 0, bad
+    n, dm, dff, blk = 300, 128, 256, 128
+    ws = ra.ring_attn_ffn_workspace_bytes(n, dm, dff, blk)
+
+    def call(**kw):
+        a = dict(x=FAKE, w1=FAKE * 8, b1=FAKE * 16, w2=FAKE * 24, b2=FAKE * 32, y=FAKE * 40, n=n, dm=dm, dff=dff,
+                 blk=blk, act=0, ws=FAKE * 48, ws_bytes=ws)
+        a.update(kw)
+        return L.ring_attn_ffn(a["x"], a["w1"], a["b1"], a["w2"], a["b2"], a["y"], a["n"], a["dm"], a["dff"], a["blk"],
+                               a["act"], a["ws"], a["ws_bytes"], None)
+    assert call(ws_bytes=ws - 1) == -4
+    assert call(act=2) == -1 and call(act=-1) == -1
+    assert call(dm=96) == -1 and call(dff=100) == -1 and call(blk=0) == -1 and call(n=-5) == -1
+    assert call(w1=None) == -1 and call(b2=None) == -1 and call(ws=None) == -1
+    assert call(y=FAKE + 2) == -1       # y overlaps x without being x
+    assert call(y=FAKE * 8) == -1       # y aliases w1
+    assert call(ws=FAKE * 24) == -1     # workspace aliases w2
+    assert call(n=0) == 0               # nothing to do
