@@ -12,11 +12,13 @@ workloads are reported under "extra" in the same JSON line: the striped grouped-
 32 query / 8 key-value heads), the same inputs under zigzag sharding, the contiguous one (S=32768, 32 heads, values scaled by 0.5) and one
 device's share of a 32-device ring over S=1048576 (8 heads), and the backward ring (gradients for a
 seeded output gradient, ``ring_attn_bwd_local``) of the non-causal 16k and the striped and zigzag causal
-64k workloads; each runs about 1 s of warm-up and 2 s of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
+64k workloads, and the blockwise feed-forward after attention (``ring_attn_ffn``: 16384 tokens of
+d_model 1024, and 4096 tokens of d_model 4096, d_ff = 4 d_model, gelu); each runs about 1 s of warm-up and 2 s of timed calls.  Every workload also reports the GFX clock amdsmi reads under that load and the
 fraction of the dense bf16 MFMA rate at that clock.
 
 FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
-runs count only the visible pairs; the backward counts 10*D (five products of that size).  Printed on stdout: one JSON line.  Progress goes to stderr.
+runs count only the visible pairs; the backward counts 10*D (five products of that size); the
+feed-forward 4 d_model d_ff per token (two products).  Printed on stdout: one JSON line.  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -246,6 +248,74 @@ def run_backward_workload(w, measure_clock=True):
     return res
 
 
+def run_ffn_workload(w, measure_clock=True):
+    """The blockwise feed-forward of workload ``w`` (``ring_attn_ffn``): about 1 s of warm-up and 2 s of
+    timed calls between HIP events on one stream.  The same two products through torch (hipBLASLt, with a
+    separate gelu kernel in between) are timed beside it as context."""
+    import numpy as np
+    import torch
+
+    import blockwise_ring_attention_step_amd as ra
+    import synth_inputs as si
+
+    t0 = time.time()
+    x, w1, b1, w2, b2 = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+                         for a in si.ffn_inputs(w.seed, w.tokens, w.d_model, w.d_ff))
+    y = torch.empty_like(x)
+    ws = torch.empty(ra.ring_attn_ffn_workspace_bytes(w.tokens, w.d_model, w.d_ff, w.block_tokens), dtype=torch.uint8,
+                     device="cuda")
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs generated and uploaded in {time.time() - t0:.1f}s")
+
+    def call():
+        ra.ring_attn_ffn(x, w1, b1, w2, b2, y, ws, block_tokens=w.block_tokens, activation=w.activation, stream=cs)
+
+    def timed(fn, stream):
+        fn()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        fn()
+        torch.cuda.synchronize()
+        one = max(time.time() - t1, 1e-4)
+        warmup = max(3, min(200, int(1.0 / one)))
+        steps = max(3, min(200, int(2.0 / one)))
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        bounds = [ra.HipEvent() for _ in range(steps + 1)]
+        bounds[0].record(stream)
+        for i in range(steps):
+            fn()
+            bounds[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_call = sorted(bounds[i].elapsed_ms(bounds[i + 1]) for i in range(steps))
+        return bounds[0].elapsed_ms(bounds[-1]) / steps, per_call, steps, warmup
+
+    ms, per_call, steps, warmup = timed(call, cs)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms:.3f} ms/call, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
+    if sclk:
+        log(f"{w.name}: GFX clock under this load {sclk:.0f} MHz (GPU busy for ~{100 * busy:.0f}% of the sampling)")
+
+    def library():
+        with torch.cuda.stream(cs):
+            h = torch.nn.functional.gelu(torch.addmm(b1, x, w1.t()), approximate="none")
+            torch.addmm(b2, h, w2.t(), out=y)
+
+    lib_ms = timed(library, cs)[0] if w.activation == "gelu" else None
+    if lib_ms:
+        log(f"{w.name}: torch (hipBLASLt + separate gelu) {lib_ms:.3f} ms/call, "
+            f"{w.flops() / (lib_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
+               ms_min=per_call[0], tflops=tflops, flops=w.flops(), kernel_tflops=None, sclk_mhz=sclk,
+               sclk_busy=busy, torch_ms=lib_ms)
+    del x, w1, b1, w2, b2, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def sample_sclk(call, torch, ms_per_call, seconds=1.2):
     """(median GFX clock in MHz, GPU busy fraction) while the same calls keep the GPU busy: a
     background thread reads amdsmi every 10 ms while this thread keeps enqueuing calls for
@@ -358,7 +428,7 @@ def main():
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
     ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
-                    "bwd_noncausal_16k,bwd_causal_striped_64k,bwd_causal_zigzag_64k",
+                    "bwd_noncausal_16k,bwd_causal_striped_64k,bwd_causal_zigzag_64k,ffn_16k,ffn_32h_4k",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -392,6 +462,19 @@ def main():
     main_res = run_workload(w, args.steps, args.warmup, not args.no_clock)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
+        if name in si.FFN_WORKLOADS:
+            wf = si.FFN_WORKLOADS[name]
+            r = run_ffn_workload(wf, not args.no_clock)
+            extras.append({"workload": name, "value": r["tflops"], "unit": "TFLOP/s", "steps": r["steps"],
+                           "warmup": r["warmup"], "ms_per_step": r["ms"], "ms_per_step_median": r["ms_median"],
+                           "ms_per_step_min": r["ms_min"], "pct_of_peak": 100 * r["tflops"] / PEAK_BF16_TFLOPS,
+                           "sclk_mhz": r["sclk_mhz"], "sclk_gpu_busy": r["sclk_busy"],
+                           "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"])
+                                                   if r["sclk_mhz"] else None),
+                           "pass": "feed-forward", "tokens": wf.tokens, "d_model": wf.d_model, "d_ff": wf.d_ff,
+                           "block_tokens": wf.block_tokens, "activation": wf.activation,
+                           "torch_reference_ms": r["torch_ms"]})
+            continue
         wx = si.WORKLOADS[name]
         r = (run_backward_workload(wx, not args.no_clock) if wx.backward
              else run_workload(wx, None, None, not args.no_clock))

@@ -103,7 +103,8 @@ def test_ffn_activation_elementwise(gpu_lib, activation):
     """Identity weights and zero biases make y = bf16(act(x)) exactly (each sum has one nonzero term of
     weight 1): the activation itself, element by element, against the oracle's rounded to bf16.  The
     kernel evaluates gelu in fp32 (erfc to a relative 1.2e-7), so a value within that of a bf16
-    rounding boundary may land one bf16 step away; everything else is bit-equal."""
+    rounding boundary may land one bf16 step away; everything else is bit-equal down to the
+    subnormal range."""
     d = 128
     n = 4096
     vals = np.concatenate([np.linspace(-10, 10, n * d // 2, dtype=np.float32),
@@ -120,7 +121,10 @@ def test_ffn_activation_elementwise(gpu_lib, activation):
     # the same sign, and at most one step apart in the bit pattern (bf16 values of one sign are ordered)
     same_sign = (got >> 15) == (want >> 15)
     diff = np.abs(got - want)
-    ok = (same_sign & (diff <= 1)) | ((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+    # zeros and subnormals (exponent field 0: |gelu| < 2^-126, far tail z < -13) count as one class:
+    # whether fp32 arithmetic keeps or flushes such values is not part of the definition
+    tiny = ((got & 0x7F80) == 0) & ((want & 0x7F80) == 0)
+    ok = (same_sign & (diff <= 1)) | tiny
     print(f"[ffn] {activation} elementwise: {np.mean(diff == 0) * 100:.3f}% bit-equal, max step {diff.max()}", flush=True)
     assert ok.all()
     assert np.mean(diff == 0) >= 0.99
