@@ -197,6 +197,15 @@ hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream, hipEvent_t 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RA_OK : RA_ERR_HIP; }
 
+// Some non-null pointer is not a multiple of `align` bytes.  The kernels move 16-byte vectors of
+// the tensors (and per-row scalars of the fp32 row arrays), so tensors must be 16-byte aligned and
+// row arrays 4-byte aligned.
+bool misaligned(std::initializer_list<const void*> ps, uintptr_t align) {
+  for (const void* p : ps)
+    if (p && (uintptr_t)p % align) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +265,7 @@ int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, fl
   const size_t rows = (size_t)n_dev * B * Hq * Nq;
   if (rows > 0 && (!q || !o_acc || !m || !l)) return RA_ERR_INVALID_ARG;
   if (kv_bytes > 0 && (!k || !v)) return RA_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, o_acc}, 16) || misaligned({m, l}, 4)) return RA_ERR_INVALID_ARG;
   // the state is written: it may not alias the inputs or itself
   const void* outs[3] = {o_acc, m, l};
   const size_t out_sz[3] = {rows * D * 4, rows * 4, rows * 4};
@@ -321,6 +331,7 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
   const size_t rows = (size_t)n_dev * B * Hq * Nq;
   if (rows == 0) return RA_OK;
   if (!o_acc || !m || !l || !o) return RA_ERR_INVALID_ARG;
+  if (misaligned({o_acc, o}, 16) || misaligned({m, l, lse}, 4)) return RA_ERR_INVALID_ARG;
   const size_t o_bytes = rows * D * elem_size(out_dtype);
   if (overlaps(o, o_bytes, o_acc, rows * D * 4) || overlaps(o, o_bytes, m, rows * 4) ||
       overlaps(o, o_bytes, l, rows * 4) || overlaps(lse, rows * 4, o, o_bytes) ||
@@ -353,6 +364,7 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
   if (n == 0) return RA_OK;
   if (!q_local || !k_src || !v_src || !o || !workspace) return RA_ERR_INVALID_ARG;
+  if (misaligned({q_local, k_src, v_src, o, workspace}, 16) || misaligned({lse}, 4)) return RA_ERR_INVALID_ARG;
   const size_t need = ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype);
   if (need == 0) return RA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RA_ERR_WORKSPACE;
@@ -603,6 +615,7 @@ int ring_attn_bwd_prep(const void* o, const void* dout, const float* lse, float*
   const size_t rows = (size_t)n_dev * B * Hq * Nq;
   if (rows == 0) return RA_OK;
   if (!o || !dout || !lse || !delta || !lse2) return RA_ERR_INVALID_ARG;
+  if (misaligned({o, dout}, 16) || misaligned({lse, delta, lse2}, 4)) return RA_ERR_INVALID_ARG;
   const size_t in_bytes = rows * D * elem_size(dtype);
   const void* ins[3] = {o, dout, lse};
   const size_t in_sz[3] = {in_bytes, in_bytes, rows * 4};
@@ -629,6 +642,7 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
   if (qrows + krows == 0) return RA_OK;
   if ((qrows > 0 && (!q || !dout || !lse2 || !delta || !dq)) || (krows > 0 && (!k || !v || !dk || !dv)))
     return RA_ERR_INVALID_ARG;
+  if (misaligned({q, k, v, dout, dq, dk, dv}, 16) || misaligned({lse2, delta}, 4)) return RA_ERR_INVALID_ARG;
   // the gradients are written: they may not alias the inputs or each other
   const void* outs[3] = {dq, dk, dv};
   const size_t out_sz[3] = {qrows * D * 4, krows * D * 4, krows * D * 4};
@@ -714,6 +728,9 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   if (layout == RA_LAYOUT_ZIGZAG && n % 2) return RA_ERR_INVALID_ARG;
   if (n == 0) return RA_OK;
   if (!q_local || !k_src || !v_src || !o_local || !dout_local || !lse_local || !dq_local || !dk || !dv || !workspace)
+    return RA_ERR_INVALID_ARG;
+  if (misaligned({q_local, k_src, v_src, o_local, dout_local, dq_local, dk, dv, workspace}, 16) ||
+      misaligned({lse_local}, 4))
     return RA_ERR_INVALID_ARG;
   const size_t need = ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype);
   if (need == 0) return RA_ERR_INVALID_ARG;
@@ -934,6 +951,7 @@ int ring_attn_ffn(const void* x, const void* w1, const void* b1, const void* w2,
   if (mul_sizes({n_tokens, d_model, 2}) < 0) return RA_ERR_INVALID_ARG;
   if (n_tokens == 0) return RA_OK;
   if (!x || !w1 || !b1 || !w2 || !b2 || !y || !workspace) return RA_ERR_INVALID_ARG;
+  if (misaligned({x, w1, w2, y, workspace}, 16) || misaligned({b1, b2}, 8)) return RA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RA_ERR_WORKSPACE;
   const size_t act_bytes = (size_t)n_tokens * d_model * 2;
   const size_t w_bytes = (size_t)d_ff * d_model * 2;

@@ -20,6 +20,9 @@
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller, except where marked "host".
  *     The caller keeps them alive until the work enqueued on the given stream(s) has completed.
+ *     Tensors (q, k, v, outputs, gradients, fp32 accumulators, workspaces) are 16-byte aligned and
+ *     per-row fp32 arrays (m, l, lse, lse2, delta) 4-byte aligned (biases of ring_attn_ffn 8-byte);
+ *     a misaligned non-null pointer is RA_ERR_INVALID_ARG.
  *   - `stream` arguments are hipStream_t values passed as void* (NULL = the default stream).
  *     Every call only enqueues work and returns; kernel faults surface at the caller's
  *     synchronisation.  Launch failures are reported as RA_ERR_HIP.

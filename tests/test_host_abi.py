@@ -264,3 +264,28 @@ def test_ffn_workspace_and_rejects_bad_arguments():
     assert call(y=FAKE * 8) == -1       # y aliases w1
     assert call(ws=FAKE * 24) == -1     # workspace aliases w2
     assert call(n=0) == 0               # nothing to do
+
+
+def test_misaligned_pointers_are_rejected():
+    L = ra.lib()
+    off = (ctypes.c_int64 * 1)(0)
+    # ring_attn_step: q 2 bytes off a 16-byte boundary; m 4-byte aligned is fine, 2-byte is not
+    step = L.ring_attn_step
+    base = dict(q=FAKE, k=FAKE * 8, v=FAKE * 16, o=FAKE * 24, m=FAKE * 40, l=FAKE * 48)
+
+    def call_step(**kw):
+        a = dict(base, **kw)
+        return step(a["q"], a["k"], a["v"], a["o"], a["m"], a["l"], 1, 1, 2, 1, 8, 8, 128, 1, 0.1, 0, off, 1,
+                    off, 1, 0, None)
+    assert call_step(q=FAKE + 2) == -1 and call_step(o=FAKE * 24 + 8) == -1 and call_step(m=FAKE * 40 + 2) == -1
+    # the feed-forward: biases need 8 bytes, tensors 16
+    n, dm, dff, blk = 300, 128, 256, 128
+    ws = ra.ring_attn_ffn_workspace_bytes(n, dm, dff, blk)
+
+    def call_ffn(**kw):
+        a = dict(x=FAKE, w1=FAKE * 8, b1=FAKE * 16, w2=FAKE * 24, b2=FAKE * 32, y=FAKE * 40, ws=FAKE * 48)
+        a.update(kw)
+        return L.ring_attn_ffn(a["x"], a["w1"], a["b1"], a["w2"], a["b2"], a["y"], n, dm, dff, blk, 0, a["ws"], ws,
+                               None)
+    assert call_ffn(w1=FAKE * 8 + 8) == -1 and call_ffn(b1=FAKE * 16 + 4) == -1 and call_ffn(ws=FAKE * 48 + 16 + 4) == -1
+    assert L.ring_attn_bwd_prep(FAKE + 4, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 1, 2, 4, 16, 0, None) == -1
