@@ -66,8 +66,8 @@ __device__ __forceinline__ float activate(float z) {
   return z;
 }
 
-template <int BM, int BN, int BK, int S, int ACT>
-__global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_bf16(const FfnGemmParams p) {
+template <int BM, int BN, int BK, int S, int ACT, int OCC>
+__global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmParams p) {
   constexpr int R = BK * 2;                  // bytes of one row of a step
   constexpr int C = R / 16;                  // 16-byte chunks per row
   constexpr int RPP = 1024 / R;              // rows per 1 KiB copy
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_bf16(const FfnGemmPar
   // that no step reads, and the fragments read for a step past the last one are not used.
   constexpr int kProducts = NB * MB;
   constexpr int kReads = NB + MB;
-  static_assert(kReads < kProducts, "one fragment read per product slot");
+  static_assert(kProducts >= 4, "slots for the barrier, reads and copies");
   auto step = [&](int s) {
     const int buf = s % S;
 #pragma unroll
@@ -221,12 +221,16 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_bf16(const FfnGemmPar
         mfma_one(set, i);
         __builtin_amdgcn_sched_barrier(0);
         if (kk + 1 < KK) {
-          if (i < kReads) read_one(buf, kk + 1, set ^ 1, i);
+#pragma unroll
+          for (int r = 0; r < kReads; ++r)
+            if (r % kProducts == i) read_one(buf, kk + 1, set ^ 1, r);
         } else if (i == 0) {
           wait_vmem<(S - 2) * kPieces>();  // step s+1 has landed (this wave's copies)
           __syncthreads();                 // ... every wave's, and every wave has read all of step s
         } else {
-          if (i <= kReads) read_one((s + 1) % S, 0, 0, i - 1);
+#pragma unroll
+          for (int r = 0; r < kReads; ++r)
+            if (1 + r % (kProducts - 1) == i) read_one((s + 1) % S, 0, 0, r);
 #pragma unroll
           for (int k = 0; k < kPieces; ++k)
             if (1 + k * (kProducts - 1) / kPieces == i) issue_piece(k, buf);
@@ -273,17 +277,27 @@ int cu_count() {
   return n;
 }
 
-template <int BM, int BN, int BK, int S, int ACT>
+// OCC workgroups per CU (1 for 256 x 256 tiles: 512 registers per lane; 2 for 128 x 128)
+template <int BM, int BN, int BK, int S, int ACT, int OCC>
 hipError_t launch_tiles(FfnGemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const int T = p.tiles_m * p.tiles_n;
-  // one workgroup per CU; when the tiles outnumber the workgroups, a multiple of 8 of them so that
-  // every round of tiles keeps the XCD of each virtual index
-  int G = std::min(T, cu_count());
+  // persistent workgroups, OCC per CU; when the tiles outnumber them, a multiple of 8 so that every
+  // round of tiles keeps the XCD of each virtual index
+  int G = std::min(T, OCC * cu_count());
   if (G < T) G = std::max(8, G / 8 * 8);
-  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, BK, S, ACT>), dim3(G), dim3(kFfnThreads), 0, stream, p);
+  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, BK, S, ACT, OCC>), dim3(G), dim3(kFfnThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// 256 x 256 tiles when they fill every CU, else 128 x 128 (four times as many, two workgroups per
+// CU): small token blocks and the narrow second projection keep the chip busy
+template <int ACT>
+hipError_t launch_act(const FfnGemmParams& p, hipStream_t stream) {
+  const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big >= cu_count()) return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, ACT, 1>(p, stream);
+  return launch_tiles<128, 128, kFfnBK, kFfnStages, ACT, 2>(p, stream);
 }
 
 }  // namespace
@@ -291,9 +305,9 @@ hipError_t launch_tiles(FfnGemmParams p, hipStream_t stream) {
 hipError_t launch_ffn_gemm_bf16(const FfnGemmParams& p, int act, hipStream_t stream) {
   if (p.M <= 0) return hipSuccess;
   switch (act) {
-    case kFfnActNone: return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, kFfnActNone>(p, stream);
-    case RA_FFN_GELU: return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, RA_FFN_GELU>(p, stream);
-    case RA_FFN_RELU: return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, RA_FFN_RELU>(p, stream);
+    case kFfnActNone: return launch_act<kFfnActNone>(p, stream);
+    case RA_FFN_GELU: return launch_act<RA_FFN_GELU>(p, stream);
+    case RA_FFN_RELU: return launch_act<RA_FFN_RELU>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
