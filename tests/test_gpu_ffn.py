@@ -128,3 +128,13 @@ def test_ffn_activation_elementwise(gpu_lib, activation):
     print(f"[ffn] {activation} elementwise: {np.mean(diff == 0) * 100:.3f}% bit-equal, max step {diff.max()}", flush=True)
     assert ok.all()
     assert np.mean(diff == 0) >= 0.99
+
+
+def test_ffn_tile_shapes_give_the_same_bits(gpu_lib):
+    """Blocks of all 16384 tokens run both projections on 256 x 256 tiles, blocks of 2048 on 128 x 128
+    tiles (too few large tiles to fill the CUs): every output is the same k-ordered sum either way."""
+    w = si.FFN_WORKLOADS["ffn_16k"]
+    dev, _ = _upload(w.seed, w.tokens, w.d_model, w.d_ff)
+    big = _run(gpu_lib, dev, 16384, "gelu")
+    small = _run(gpu_lib, dev, 2048, "gelu")
+    assert torch.equal(big, small)
