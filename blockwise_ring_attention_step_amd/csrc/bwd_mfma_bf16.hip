@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 // bwd_dkv: 128 keys per workgroup, 8 waves, two per SIMD.  Waves w and w + 4 share the keys
 // 32 (w % 4) .. + 31 and split the work, so that each holds one gradient accumulator and two waves
 // fit every SIMD.  Per query tile, in two halves separated by a workgroup barrier:
-//   value wave (w < 4): S = Q K^T, P = 2^(x - lse2) (kept as bf16, and stored to LDS in fp32) |
+//   value wave (w < 4): S = Q K^T, P = 2^(x - lse2) (kept as bf16, and stored to LDS as bf16) |
 //                       dV^T += dO^T P
 //   key wave (w >= 4):  dP = dO V^T                                                         |
 //                       dS = P (from LDS) * (dP - delta), dK^T += Q^T dS
@@ -305,7 +305,7 @@ constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvKeys = 32 * (kKvWaves / 2);
 constexpr int kKvStageBytes = 2 * kTileBytes + 512;  // Q tile, dO tile, lse2 (256 B) + delta (256 B)
-constexpr int kKvPBytes = 4 * 2 * 64 * 64;           // P in fp32: 4 wave pairs x 2 halves x 64 lanes x 64 B
+constexpr int kKvPBytes = 4 * 4 * 64 * 16;           // P in bf16: 4 wave pairs x 4 packs x 64 lanes x 16 B
 constexpr int kKvPieces = 16 / kKvWaves;             // 1 KiB pieces per wave per Q (and per dO) tile
 
 struct KvCtx {
@@ -342,8 +342,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool key_wave = wave >= kKvWaves / 2;  // accumulates dK (else dV)
-  // this pair's P buffer: [half][group g][lane] f32x4 (registers 4 g .. 4 g + 3 of the lane)
-  LDS_AS f32x4* pbuf = (LDS_AS f32x4*)(smem + kBwdStages * kKvStageBytes) + (wave & 3) * 2 * 4 * 64;
+  // this pair's P buffer: [pack][lane] bf16x8; pack 2 c2 + hh holds registers 8 hh .. 8 hh + 7 of the
+  // 32-row half c2 (the accumulator layout of S and dP, whose lane is the key)
+  LDS_AS i16x8* pbuf = (LDS_AS i16x8*)(smem + kBwdStages * kKvStageBytes) + (wave & 3) * 4 * 64;
   const int j = lane & 31, h2 = lane >> 5;
 
   // work item: (slot, batch, key/value head, key tile of 128); the key tiles of one (slot, batch,
@@ -463,9 +464,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
               if (row < qmin_lane || row >= Nq) t2[c2][r] = 0.f;
             }
           }
+          float x[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            pbuf[(c2 * 4 + g) * 64 + lane] = f32x4{t2[c2][4 * g], t2[c2][4 * g + 1], t2[c2][4 * g + 2], t2[c2][4 * g + 3]};
+          for (int r = 0; r < 16; ++r) x[r] = t2[c2][r];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) pbuf[(2 * c2 + hh) * 64 + lane] = __builtin_bit_cast(i16x8, pack_half(x, hh));
         }
       } else {
 #pragma unroll
@@ -498,11 +501,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
         for (int c2 = 0; c2 < 2; ++c2) {
           float x[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 p4 = pbuf[(c2 * 4 + g) * 64 + lane];
-            const f32x4 d4 = *(const LDS_AS f32x4*)(dell + 32 * c2 + 8 * g + 4 * h2);
+          for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8 p8 = __builtin_bit_cast(bf16x8, pbuf[(2 * c2 + hh) * 64 + lane]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[4 * g + i] = p4[i] * (t2[c2][4 * g + i] - d4[i]);
+            for (int g2 = 0; g2 < 2; ++g2) {
+              const int g = 2 * hh + g2;
+              const f32x4 d4 = *(const LDS_AS f32x4*)(dell + 32 * c2 + 8 * g + 4 * h2);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) x[4 * g + i] = (float)p8[4 * g2 + i] * (t2[c2][4 * g + i] - d4[i]);
+            }
           }
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
