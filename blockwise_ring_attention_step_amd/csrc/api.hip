@@ -938,7 +938,7 @@ size_t ring_attn_ffn_workspace_bytes(int64_t n_tokens, int d_model, int d_ff, in
   if (n_tokens < 0 || block_tokens < 1) return 0;
   if (d_model < 64 || d_model > 65536 || d_model % 64 || d_ff < 64 || d_ff > 65536 || d_ff % 64) return 0;
   const int64_t rows = std::max<int64_t>(1, std::min(n_tokens, block_tokens));  // one block's tokens
-  if (rows > INT32_MAX) return 0;
+  if (rows > ((int64_t)1 << 30)) return 0;  // keeps the kernels' 32-bit row indices (row + tile) in range
   return (size_t)rows * d_ff * 2;
 }
 

@@ -267,7 +267,8 @@ size_t ring_attn_bwd_local_workspace_bytes(int P, int n_local, int B, int Hq, in
  *   w2     [d_model, d_ff] bf16         b2 [d_model] bf16   one row per output feature)
  *   y      [n_tokens, d_model] bf16 out  may be x itself (in place); no other overlap
  *   block_tokens  tokens per block (>= 1): one block's hidden activations act(x W1^T + b1),
- *                 [min(block_tokens, n_tokens), d_ff] bf16, live in the workspace
+ *                 [min(block_tokens, n_tokens), d_ff] bf16, live in the workspace; at most 2^30
+ *                 tokens per block
  *   activation    RA_FFN_GELU or RA_FFN_RELU
  *   workspace     device memory, >= ring_attn_ffn_workspace_bytes(...)
  * d_model and d_ff are multiples of 64 in [64, 65536].  Products accumulate in fp32; the hidden

@@ -245,7 +245,7 @@ def test_ffn_workspace_and_rejects_bad_arguments():
     assert ra.ring_attn_ffn_workspace_bytes(100, 128, 512, 256) == 100 * 512 * 2   # one block of all tokens
     assert ra.ring_attn_ffn_workspace_bytes(0, 128, 512, 256) == 512 * 2
     for bad in ((10, 96, 512, 4), (10, 128, 500, 4), (10, 128, 512, 0), (-1, 128, 512, 4), (10, 0, 512, 4),
-                (10, 128, 65600, 4), (1 << 40, 128, 64, 1 << 40)):
+                (10, 128, 65600, 4), (1 << 40, 128, 64, 1 << 40), ((1 << 30) + 1, 64, 64, 1 << 31)):
         assert ra.ring_attn_ffn_workspace_bytes(*bad) == 0, bad
     n, dm, dff, blk = 300, 128, 256, 128
     ws = ra.ring_attn_ffn_workspace_bytes(n, dm, dff, blk)
