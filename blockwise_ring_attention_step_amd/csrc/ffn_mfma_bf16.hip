@@ -8,8 +8,9 @@
 // a [M, K] (tokens x features, row-major), w [N, K] (the weight in nn.Linear layout: one row per
 // output feature), both read along k.
 //
-// A workgroup of 4 waves (one per SIMD, 256 accumulator registers each) owns BM x BN output tiles,
-// one after the other (persistent: one workgroup per CU); each wave a (BM/2) x (BN/2) quarter as
+// A workgroup of 4 waves (one per SIMD, 256 accumulator registers each for 256 x 256 tiles) owns
+// BM x BN output tiles, one after the other (persistent: one workgroup per CU, or two with the
+// 128 x 128 tiles taken when the large ones would leave CUs idle); each wave a (BM/2) x (BN/2) quarter as
 // (BN/64) x (BM/64) accumulators of 32 x 32, held transposed (the lane is the token m, the register
 // the feature n, so that 4 consecutive features leave as one 8-byte store).  k advances in steps of
 // BK: the a and w rows of a step go HBM -> LDS directly (global_load_lds) into a ring of S buffers.
