@@ -60,7 +60,9 @@ def unshard_lse(lse: np.ndarray, layout: str) -> np.ndarray:
 
 def run_ring_local(q, k, v, *, P, causal, layout, dtype, dev0=0, n_local=None, scale=None, host_kv=False,
                    two_streams=True):
-    """q [B, S or n_local*n, Hq, D], k/v [B, S, Hkv, D] (token order; bits for bf16).
+    """q [B, S or n_local*n, Hq, D], k/v [B, S, Hkv, D] (token order; bits for bf16).  A q with S rows
+    is in token order and is sharded here; a q with n_local*n < S rows holds the local devices' rows
+    already in shard order (so a full local ring takes q in token order).
 
     Runs ring_attn_local for devices [dev0, dev0+n_local) and returns (o [P_local, B, n, Hq, D] float64
     in shard order, lse [P_local, B, Hq, n])."""

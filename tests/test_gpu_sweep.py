@@ -1,0 +1,158 @@
+"""Seeded random sweep of shapes through the C ABI against the float64 oracle: the forward ring
+(bf16 MFMA path and the fp32 / other-head-size path), the backward ring and the feed-forward, with
+ring sizes, ragged shard lengths, grouped-query ratios, layouts, masks and partly local rings drawn
+from a fixed seed.  The draws are printed before each case runs, so a failure names its shape.
+Tolerances as in the other GPU tests (fp32 1e-5; bf16 output 2e-2 and LSE 1e-3; gradients
+2e-2 / 1e-2 of the reference scale; feed-forward 1e-2 / 5e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_ring_attention_step_amd as ra
+import oracle
+import synth_inputs as si
+from ring_harness import TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_err, run_ring_local, shard, to_device, to_float
+
+pytestmark = pytest.mark.gpu
+
+RNG_SEED = 20261203
+
+
+def _draw_forward(rng, mfma):
+    P = int(rng.choice([2, 3, 4, 5, 8]))
+    layout = str(rng.choice(["contiguous", "striped", "zigzag"]))
+    n = int(rng.integers(1, 200))
+    if layout == "zigzag":
+        n += n % 2
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    D = 128 if mfma else int(rng.choice([16, 32, 48, 64, 80, 128]))
+    causal = bool(rng.integers(0, 2))
+    n_local = int(rng.integers(1, P + 1))
+    dev0 = int(rng.integers(0, P - n_local + 1))
+    return dict(P=P, n=n, Hq=Hq, Hkv=Hkv, D=D, causal=causal, layout=layout, dev0=dev0, n_local=n_local)
+
+
+def _forward_cases(count, mfma, offset):
+    rng = np.random.default_rng(RNG_SEED + offset)
+    return [_draw_forward(rng, mfma) for _ in range(count)]
+
+
+def _check_forward(c, dtype, seed):
+    print(f"[sweep] forward {dtype} {c}", flush=True)
+    P, n, Hq, Hkv, D = c["P"], c["n"], c["Hq"], c["Hkv"], c["D"]
+    S = P * n
+    gen = si.normal_bf16 if dtype == "bf16" else si.normal_f32
+    q, k, v = gen(seed, (1, S, Hq, D)), gen(seed + 1, (1, S, Hkv, D)), gen(seed + 2, (1, S, Hkv, D))
+    pos = oracle.shard_positions(S, P, c["layout"])
+    local = pos[c["dev0"]:c["dev0"] + c["n_local"]]
+    # q in token order: the harness shards it and keeps the local devices' shards
+    o, lse = run_ring_local(q, k, v, P=P, causal=c["causal"], layout=c["layout"], dtype=dtype, dev0=c["dev0"],
+                            n_local=c["n_local"])
+    rows = np.array([[0, h, int(local[t, r])] for t in range(c["n_local"]) for h in range(Hq) for r in range(n)])
+    ref_o, ref_lse = oracle.attention_rows(to_float(q, dtype), to_float(k, dtype), to_float(v, dtype), rows,
+                                           causal=c["causal"])
+    got_o = np.concatenate([o[t, 0].transpose(1, 0, 2).reshape(-1, D) for t in range(c["n_local"])])
+    got_lse = np.concatenate([lse[t, 0].reshape(-1) for t in range(c["n_local"])])
+    eo, el = max_err(got_o, ref_o), max_err(got_lse, ref_lse)
+    print(f"[sweep]   max|dO|={eo:.3g} max|dLSE|={el:.3g}", flush=True)
+    tol_o, tol_l = (TOL_BF16_O, TOL_BF16_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    assert eo <= tol_o and el <= tol_l
+
+
+@pytest.mark.parametrize("i,c", list(enumerate(_forward_cases(10, True, 0))))
+def test_sweep_forward_bf16(gpu_lib, i, c):
+    _check_forward(c, "bf16", 31000 + 10 * i)
+
+
+@pytest.mark.parametrize("i,c", list(enumerate(_forward_cases(6, False, 1))))
+def test_sweep_forward_fp32(gpu_lib, i, c):
+    _check_forward(c, "f32", 32000 + 10 * i)
+
+
+def _backward_cases(count):
+    rng = np.random.default_rng(RNG_SEED + 2)
+    return [_draw_forward(rng, True) for _ in range(count)]
+
+
+@pytest.mark.parametrize("i,c", list(enumerate(_backward_cases(6))))
+def test_sweep_backward(gpu_lib, i, c):
+    print(f"[sweep] backward {c}", flush=True)
+    P, n, Hq, Hkv, D, layout = c["P"], c["n"], c["Hq"], c["Hkv"], c["D"], c["layout"]
+    dev0, n_local = c["dev0"], c["n_local"]
+    S = P * n
+    seed = 33000 + 10 * i
+    q, k, v, do = (si.normal_bf16(seed + j, (1, S, H, D)) for j, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    scale = 1.0 / math.sqrt(D)
+    tq = to_device(shard(q, P, layout)[dev0:dev0 + n_local], "bf16")
+    tdo = to_device(shard(do, P, layout)[dev0:dev0 + n_local], "bf16")
+    tk, tv = to_device(shard(k, P, layout), "bf16"), to_device(shard(v, P, layout), "bf16")
+    o = torch.empty_like(tq)
+    lse = torch.empty((n_local, 1, Hq, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(P, n_local, 1, Hq, Hkv, n, D, ra.RA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    xs = torch.cuda.Stream()
+    ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=P, dev0=dev0, scale=scale, causal=c["causal"], layout=layout,
+                       copy_stream=xs)
+    dq = torch.full(tq.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full(tk.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dv = torch.full(tk.shape, float("nan"), dtype=torch.float32, device="cuda")
+    wsb = torch.empty(ra.ring_attn_bwd_local_workspace_bytes(P, n_local, 1, Hq, Hkv, n, D, ra.RA_BF16),
+                      dtype=torch.uint8, device="cuda")
+    ra.ring_attn_bwd_local(tq, tk, tv, o, tdo, lse, dq, dk, dv, wsb, P=P, dev0=dev0, scale=scale, causal=c["causal"],
+                           layout=layout, copy_stream=xs)
+    torch.cuda.synchronize()
+    qf, kf, vf, dof = (to_float(x, "bf16") for x in (q, k, v, do))
+    pos = oracle.shard_positions(S, P, layout)
+    local_tok = pos[dev0:dev0 + n_local].reshape(-1)
+    keep = np.zeros(S, bool)
+    keep[local_tok] = True
+    dof = np.where(keep[None, :, None, None], dof, 0.0)  # only the local queries' gradients flow
+    rq, rk, rv = oracle.attention_backward_reference(qf, kf, vf, dof, causal=c["causal"])
+    f = lambda t: t.cpu().numpy().astype(np.float64)
+    got_q = f(dq).transpose(1, 0, 2, 3, 4).reshape(1, n_local * n, Hq, D)
+    perm = pos.reshape(-1)
+
+    def tok(x):
+        flat = x.transpose(1, 0, 2, 3, 4).reshape(1, S, Hkv, D)
+        out = np.empty_like(flat)
+        out[:, perm] = flat
+        return out
+    for name, got, ref in (("dq", got_q, rq[:, local_tok]), ("dk", tok(f(dk)), rk), ("dv", tok(f(dv)), rv)):
+        scale_ref = max(np.abs(ref).max(), 1e-30)
+        emax = np.abs(got - ref).max() / scale_ref
+        efro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        print(f"[sweep]   {name}: max {emax:.2e} fro {efro:.2e}", flush=True)
+        assert np.isfinite(emax) and emax <= 2e-2 and efro <= 1e-2, name
+
+
+def _ffn_cases(count):
+    rng = np.random.default_rng(RNG_SEED + 3)
+    out = []
+    for _ in range(count):
+        out.append(dict(tokens=int(rng.integers(1, 1500)), dm=64 * int(rng.integers(1, 9)),
+                        dff=64 * int(rng.integers(1, 25)), block=int(rng.integers(1, 1600)),
+                        act=str(rng.choice(["gelu", "relu"]))))
+    return out
+
+
+@pytest.mark.parametrize("i,c", list(enumerate(_ffn_cases(8))))
+def test_sweep_ffn(gpu_lib, i, c):
+    print(f"[sweep] ffn {c}", flush=True)
+    x, w1, b1, w2, b2 = si.ffn_inputs(34000 + 10 * i, c["tokens"], c["dm"], c["dff"])
+    dev = [to_device(a, "bf16") for a in (x, w1, b1, w2, b2)]
+    y = torch.full_like(dev[0], float("nan"))
+    ws = torch.empty(ra.ring_attn_ffn_workspace_bytes(c["tokens"], c["dm"], c["dff"], c["block"]), dtype=torch.uint8,
+                     device="cuda")
+    ra.ring_attn_ffn(*dev, y, ws, block_tokens=c["block"], activation=c["act"])
+    torch.cuda.synchronize()
+    f = lambda a: si.bf16_to_f32(a).astype(np.float64)
+    ref = oracle.ffn_reference(f(x), f(w1).T, f(b1), f(w2).T, f(b2), activation=c["act"])
+    got = y.float().cpu().numpy().astype(np.float64)
+    emax = np.abs(got - ref).max() / np.abs(ref).max()
+    efro = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"[sweep]   max {emax:.2e} fro {efro:.2e}", flush=True)
+    assert np.isfinite(emax) and emax <= 1e-2 and efro <= 5e-3
