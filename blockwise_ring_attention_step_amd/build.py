@@ -12,7 +12,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libringattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.hip", "step_mfma_bf16.hip", "step_generic.hip", "bwd_mfma_bf16.hip", "ffn_mfma_bf16.hip"]
+SOURCES = ["api.hip", "step_mfma_bf16.hip", "step_generic.hip", "bwd_mfma_bf16.hip", "bwd_generic.hip",
+           "ffn_mfma_bf16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

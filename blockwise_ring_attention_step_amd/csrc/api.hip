@@ -195,6 +195,14 @@ hipError_t launch_step(StepParams& p, int dtype, hipStream_t stream, hipEvent_t 
   return ra::launch_step_generic(p, dtype, stream, ev_start, ev_stop);
 }
 
+// One pass of a backward step launch (query gradients, or key/value gradients) on the kernel for
+// the dtype and head dim, as launch_step chooses the forward's.
+hipError_t launch_bwd(const ra::BwdParams& p, int dtype, bool dq_pass, hipStream_t stream) {
+  if (uses_mfma_kernel(dtype, p.D))
+    return dq_pass ? ra::launch_bwd_dq_bf16_d128(p, stream) : ra::launch_bwd_dkv_bf16_d128(p, stream);
+  return ra::launch_bwd_generic(p, dtype, dq_pass, stream);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? RA_OK : RA_ERR_HIP; }
 
 // Some non-null pointer is not a multiple of `align` bytes.  The kernels move 16-byte vectors of
@@ -635,7 +643,6 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
   if (flags & ~(RA_BWD_INIT_DQ | RA_BWD_INIT_DKV)) return RA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
-  if (!uses_mfma_kernel(dtype, D)) return RA_ERR_UNSUPPORTED;
   const bool causal = mask == RA_MASK_CAUSAL;
   if (causal && (!q_off || !k_off || q_stride <= 0 || k_stride <= 0)) return RA_ERR_INVALID_ARG;
   const size_t qrows = (size_t)n_dev * B * Nq * Hq, krows = (size_t)n_dev * B * Nk * Hkv;
@@ -647,7 +654,8 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
   const void* outs[3] = {dq, dk, dv};
   const size_t out_sz[3] = {qrows * D * 4, krows * D * 4, krows * D * 4};
   const void* ins[6] = {q, k, v, dout, lse2, delta};
-  const size_t in_sz[6] = {qrows * D * 2, krows * D * 2, krows * D * 2, qrows * D * 2, qrows * 4, qrows * 4};
+  const size_t es = elem_size(dtype);
+  const size_t in_sz[6] = {qrows * D * es, krows * D * es, krows * D * es, qrows * D * es, qrows * 4, qrows * 4};
   for (int a = 0; a < 3; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlaps(outs[a], out_sz[a], ins[b], in_sz[b])) return RA_ERR_INVALID_ARG;
@@ -698,9 +706,9 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
                            ((flags & RA_BWD_INIT_DKV) ? ra::kBwdInitDkv : 0));
   }
   if (p.n_launch == 0) return RA_OK;
-  rc = hip_status(ra::launch_bwd_dq_bf16_d128(p, st));
+  rc = hip_status(launch_bwd(p, dtype, true, st));
   if (rc != RA_OK) return rc;
-  return hip_status(ra::launch_bwd_dkv_bf16_d128(p, st));
+  return hip_status(launch_bwd(p, dtype, false, st));
 }
 
 size_t ring_attn_bwd_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype) {
@@ -724,7 +732,6 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
   if (!valid_layout(layout)) return RA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.f)) return RA_ERR_INVALID_ARG;
-  if (!uses_mfma_kernel(dtype, D)) return RA_ERR_UNSUPPORTED;
   if (layout == RA_LAYOUT_ZIGZAG && n % 2) return RA_ERR_INVALID_ARG;
   if (n == 0) return RA_OK;
   if (!q_local || !k_src || !v_src || !o_local || !dout_local || !lse_local || !dq_local || !dk || !dv || !workspace)
@@ -897,7 +904,7 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
           p.k_stride = un.stride;
           p.flags[x] = first_flags[(size_t)s * n_units + u];
         }
-        const hipError_t e = dq_pass ? ra::launch_bwd_dq_bf16_d128(p, cs) : ra::launch_bwd_dkv_bf16_d128(p, cs);
+        const hipError_t e = launch_bwd(p, dtype, dq_pass, cs);
         if (e != hipSuccess) return e;
       }
       return hipSuccess;

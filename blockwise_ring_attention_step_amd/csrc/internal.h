@@ -114,6 +114,8 @@ hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t strea
                                hipEvent_t ev_stop);
 hipError_t launch_bwd_dq_bf16_d128(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkv_bf16_d128(const BwdParams& p, hipStream_t stream);
+// the same two passes for every other (dtype, head dim): dq_pass selects the query-gradient kernel
+hipError_t launch_bwd_generic(const BwdParams& p, int dtype, bool dq_pass, hipStream_t stream);
 // delta[row] = sum_d dout * out and lse2[row] = log2(e) * lse[row], rows of [n_dev, B, Hq, Nq]
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2, int n_dev,
                            int B, int Hq, int Nq, int D, int dtype, hipStream_t stream);

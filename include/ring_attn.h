@@ -196,7 +196,8 @@ int64_t ring_attn_visible_pairs(int P, int n, int mask, int layout, int i, int j
  * (query block, key/value block) pair, with x = log2(e) * scale * q.k:
  *   p = 2^(x - lse2), lse2 = log2(e) * lse;  dp = dO . v;  ds = p * (dp - delta), delta = sum dO * O;
  *   dq += scale * ds k;  dk += scale * ds^T q;  dv += p^T dO.
- * Supported: bf16 with D == 128 (RA_ERR_UNSUPPORTED otherwise); gradients are fp32.
+ * Supported: bf16 or fp32 inputs, 1 <= D <= 128; gradients are fp32.  bf16 with D == 128 runs the
+ * MFMA kernels, every other case a plain fp32 kernel pair (correctness path, not tuned).
  */
 
 /*
@@ -215,8 +216,8 @@ int ring_attn_bwd_prep(const void* o, const void* dout, const float* lse, float*
  * ring_attn_bwd_step — add the gradient contributions of n_dev independent (query block, key/value
  * block) pairs: device t's queries q[t] against the block k[t], v[t], whose gradient accumulators
  * are dk[t], dv[t] (they travel with the block; the caller moves them with it).
- *   q, dout  [n_dev, B, Nq, Hq, D] bf16       lse2, delta [n_dev, B, Hq, Nq] fp32 (ring_attn_bwd_prep)
- *   k, v     [n_dev, B, Nk, Hkv, D] bf16
+ *   q, dout  [n_dev, B, Nq, Hq, D] dtype      lse2, delta [n_dev, B, Hq, Nq] fp32 (ring_attn_bwd_prep)
+ *   k, v     [n_dev, B, Nk, Hkv, D] dtype
  *   dq       [n_dev, B, Nq, Hq, D] fp32       dk, dv [n_dev, B, Nk, Hkv, D] fp32  (in/out)
  *   flags    RA_BWD_INIT_DQ | RA_BWD_INIT_DKV, or 0 to accumulate
  * Positions, masking, scale and grouped-query heads as in ring_attn_step.  Fully masked pairs launch
@@ -231,8 +232,8 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
 /*
  * ring_attn_bwd_local — the backward ring for devices [dev0, dev0 + n_local) of a P-way ring
  * (same schedule as ring_attn_local: in step s device i holds block (i - s) mod P).
- *   q_local, o_local, dout_local [n_local, B, n, Hq, D] bf16    lse_local [n_local, B, Hq, n] fp32
- *   k_src, v_src [P, B, n, Hkv, D] bf16, device memory
+ *   q_local, o_local, dout_local [n_local, B, n, Hq, D] dtype   lse_local [n_local, B, Hq, n] fp32
+ *   k_src, v_src [P, B, n, Hkv, D] dtype, device memory
  *   dq_local [n_local, B, n, Hq, D] fp32 out     gradient of the local devices' queries
  *   dk, dv   [P, B, n, Hkv, D] fp32 out          gradient of every shard's keys and values from the
  *                                                local devices' queries (the whole gradient when

@@ -10,6 +10,12 @@ forward's log-sum-exp (relative error ~1e-6) and round P and dS to bf16 for the 
 2^-9 per term).  Each gradient entry is a sum of such terms with fp32 accumulation, so its error is a
 few 2^-9 of the magnitude of its terms; bounded here by max |err| <= 2e-2 * max |ref| per tensor and
 a relative Frobenius error <= 1e-2.
+
+The other (dtype, head dim) cases run the plain fp32 kernel pair: fp32 inputs keep P, dS and every
+product in fp32 (unit roundoff 2^-24), so each gradient entry carries a few 1e-7 of the magnitude of
+its terms summed over a few hundred keys or queries; bounded by max |err| <= 1e-4 * max |ref| and a
+relative Frobenius error <= 2e-5, hundreds of times below what a dropped term or a wrong mask gives.
+bf16 inputs on that path keep the bf16 bounds above.
 """
 import math
 
@@ -26,6 +32,8 @@ pytestmark = pytest.mark.gpu
 
 TOL_MAX = 2e-2
 TOL_FRO = 1e-2
+TOL_F32_MAX = 1e-4
+TOL_F32_FRO = 2e-5
 
 
 def _unshard_kv(x, layout):
@@ -42,8 +50,8 @@ def _errors(got, ref):
     return emax, efro
 
 
-def _run_bwd(q, k, v, do, *, P, causal, layout, dev0=0, n_local=None, scale=None, two_streams=True):
-    """q/dO [B, S, Hq, D] (bf16 bits, token order), k/v [B, S, Hkv, D].  Returns (dq [n_local, B, n, Hq, D],
+def _run_bwd(q, k, v, do, *, P, causal, layout, dev0=0, n_local=None, scale=None, two_streams=True, dtype="bf16"):
+    """q/dO [B, S, Hq, D] (bf16 bits or fp32 per dtype, token order), k/v [B, S, Hkv, D].  Returns (dq [n_local, B, n, Hq, D],
     dk, dv [P, B, n, Hkv, D]) float64 in shard order, and the local query shards' token positions."""
     B, S, Hkv, D = k.shape
     Hq = q.shape[2]
@@ -52,20 +60,21 @@ def _run_bwd(q, k, v, do, *, P, causal, layout, dev0=0, n_local=None, scale=None
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     qs = shard(q, P, layout)[dev0:dev0 + n_local]
     dos = shard(do, P, layout)[dev0:dev0 + n_local]
-    tq, tdo = to_device(qs, "bf16"), to_device(dos, "bf16")
-    tk, tv = to_device(shard(k, P, layout), "bf16"), to_device(shard(v, P, layout), "bf16")
+    tq, tdo = to_device(qs, dtype), to_device(dos, dtype)
+    tk, tv = to_device(shard(k, P, layout), dtype), to_device(shard(v, P, layout), dtype)
+    code = ra.RA_BF16 if dtype == "bf16" else ra.RA_F32
     o = torch.empty_like(tq)
     lse = torch.empty((n_local, B, Hq, n), dtype=torch.float32, device="cuda")
     cs = torch.cuda.current_stream()
     xs = torch.cuda.Stream() if two_streams else None
-    ws = torch.empty(ra.ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, ra.RA_BF16), dtype=torch.uint8,
+    ws = torch.empty(ra.ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, code), dtype=torch.uint8,
                      device="cuda")
     ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=P, dev0=dev0, scale=scale, causal=causal, layout=layout,
                        copy_stream=xs)
     dq = torch.empty(tq.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(tk.shape, dtype=torch.float32, device="cuda")
-    wsb = torch.empty(ra.ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, ra.RA_BF16),
+    wsb = torch.empty(ra.ring_attn_bwd_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, code),
                       dtype=torch.uint8, device="cuda")
     # poison the outputs: every element must be written
     dq.fill_(float("nan"))
@@ -78,16 +87,16 @@ def _run_bwd(q, k, v, do, *, P, causal, layout, dev0=0, n_local=None, scale=None
     return f(dq), f(dk), f(dv)
 
 
-def _check(B, P, n, Hq, Hkv, causal, layout, seed, dev0=0, n_local=None):
+def _check(B, P, n, Hq, Hkv, causal, layout, seed, dev0=0, n_local=None, dtype="bf16", D=128):
     S = P * n
-    D = 128
-    q = si.normal_bf16(seed, (B, S, Hq, D))
-    k = si.normal_bf16(seed + 1, (B, S, Hkv, D))
-    v = si.normal_bf16(seed + 2, (B, S, Hkv, D))
-    do = si.normal_bf16(seed + 3, (B, S, Hq, D))
+    gen = si.normal_bf16 if dtype == "bf16" else si.normal_f32
+    q = gen(seed, (B, S, Hq, D))
+    k = gen(seed + 1, (B, S, Hkv, D))
+    v = gen(seed + 2, (B, S, Hkv, D))
+    do = gen(seed + 3, (B, S, Hq, D))
     n_local = P if n_local is None else n_local
-    dq, dk, dv = _run_bwd(q, k, v, do, P=P, causal=causal, layout=layout, dev0=dev0, n_local=n_local)
-    qf, kf, vf, dof = (to_float(x, "bf16") for x in (q, k, v, do))
+    dq, dk, dv = _run_bwd(q, k, v, do, P=P, causal=causal, layout=layout, dev0=dev0, n_local=n_local, dtype=dtype)
+    qf, kf, vf, dof = (to_float(x, dtype) for x in (q, k, v, do))
     pos = oracle.shard_positions(S, P, layout)
     local_tok = pos[dev0:dev0 + n_local].reshape(-1)
     if n_local < P:  # only the local queries contribute: zero the output gradient of the others
@@ -99,10 +108,12 @@ def _check(B, P, n, Hq, Hkv, causal, layout, seed, dev0=0, n_local=None):
     ref_q = rq[:, local_tok]
     got_k, got_v = _unshard_kv(dk, layout), _unshard_kv(dv, layout)
     errs = {"dq": _errors(got_q, ref_q), "dk": _errors(got_k, rk), "dv": _errors(got_v, rv)}
-    print(f"[bwd] B={B} P={P} n={n} Hq={Hq} Hkv={Hkv} causal={causal} {layout} dev0={dev0} n_local={n_local}: "
-          + " ".join(f"{k_}: max {e[0]:.2e} fro {e[1]:.2e}" for k_, e in errs.items()), flush=True)
+    print(f"[bwd] {dtype} D={D} B={B} P={P} n={n} Hq={Hq} Hkv={Hkv} causal={causal} {layout} dev0={dev0} "
+          f"n_local={n_local}: " + " ".join(f"{k_}: max {e[0]:.2e} fro {e[1]:.2e}" for k_, e in errs.items()),
+          flush=True)
+    tol_max, tol_fro = (TOL_MAX, TOL_FRO) if dtype == "bf16" else (TOL_F32_MAX, TOL_F32_FRO)
     for name, (emax, efro) in errs.items():
-        assert np.isfinite(emax) and emax <= TOL_MAX and efro <= TOL_FRO, name
+        assert np.isfinite(emax) and emax <= tol_max and efro <= tol_fro, name
 
 
 @pytest.mark.parametrize("causal,layout,n", [(False, "contiguous", 128), (True, "contiguous", 200),
@@ -169,3 +180,61 @@ def test_bwd_step_accumulates_and_splits(gpu_lib):
     for got, ref in ((dq1, rq), (dk1, rk), (dv1, rv)):
         emax, efro = _errors(got[0].cpu().numpy(), ref)
         assert emax <= TOL_MAX and efro <= TOL_FRO
+
+
+@pytest.mark.parametrize("dtype,D,causal,layout,n,dev0,n_local", [
+    ("f32", 64, True, "contiguous", 72, 0, None),
+    ("f32", 40, True, "striped", 50, 0, None),
+    ("f32", 128, True, "zigzag", 64, 0, None),   # fp32 at D = 128 also takes the plain kernels
+    ("f32", 16, False, "contiguous", 33, 1, 2),
+    ("bf16", 64, False, "contiguous", 96, 0, None),
+    ("bf16", 80, True, "zigzag", 70, 1, 2),
+])
+def test_bwd_ring_generic_kernels(gpu_lib, dtype, D, causal, layout, n, dev0, n_local):
+    """Every (dtype, head dim) other than bf16 at 128 runs the plain fp32 kernel pair."""
+    _check(2, 4, n, 4, 2, causal, layout, 1100 + D + n, dev0=dev0, n_local=n_local, dtype=dtype, D=D)
+
+
+def test_bwd_step_generic_accumulates_and_splits(gpu_lib):
+    """fp32, head dim 48: two bwd_step calls over the halves of a key block equal one call over the
+    whole block (accumulation and both INIT flags on the plain kernels), and match the oracle."""
+    B, Nq, Nk, Hq, Hkv, D = 2, 70, 90, 3, 1, 48
+    seed = 1200
+    q = to_device(si.normal_f32(seed, (1, B, Nq, Hq, D)), "f32")
+    k = to_device(si.normal_f32(seed + 1, (1, B, Nk, Hkv, D)), "f32")
+    v = to_device(si.normal_f32(seed + 2, (1, B, Nk, Hkv, D)), "f32")
+    do = to_device(si.normal_f32(seed + 3, (1, B, Nq, Hq, D)), "f32")
+    oacc = torch.zeros((1, B, Hq, Nq, D), dtype=torch.float32, device="cuda")
+    m = torch.zeros((1, B, Hq, Nq), dtype=torch.float32, device="cuda")
+    l = torch.zeros_like(m)
+    kw = dict(scale=D ** -0.5, causal=True, q_off=[Nk - Nq], k_off=[0])
+    ra.ring_attn_step(q, k, v, oacc, m, l, init=True, **kw)
+    o = torch.empty_like(q)
+    lse = torch.empty_like(m)
+    ra.ring_attn_finalize(oacc, m, l, o, lse)
+    delta, lse2 = torch.empty_like(m), torch.empty_like(m)
+    ra.ring_attn_bwd_prep(o, do, lse, delta, lse2)
+    dq1 = torch.full((1, B, Nq, Hq, D), 7.0, device="cuda")
+    dk1 = torch.full((1, B, Nk, Hkv, D), 7.0, device="cuda")
+    dv1 = torch.full_like(dk1, 7.0)
+    ra.ring_attn_bwd_step(q, k, v, do, lse2, delta, dq1, dk1, dv1, init_dq=True, init_dkv=True, **kw)
+    h = 37
+    k0, k1 = k[:, :, :h].contiguous(), k[:, :, h:].contiguous()
+    v0, v1 = v[:, :, :h].contiguous(), v[:, :, h:].contiguous()
+    dq2 = torch.full_like(dq1, 7.0)
+    dk2a, dk2b = torch.full((1, B, h, Hkv, D), 7.0, device="cuda"), torch.full((1, B, Nk - h, Hkv, D), 7.0, device="cuda")
+    dv2a, dv2b = torch.full_like(dk2a, 7.0), torch.full_like(dk2b, 7.0)
+    ra.ring_attn_bwd_step(q, k0, v0, do, lse2, delta, dq2, dk2a, dv2a, init_dq=True, init_dkv=True, **kw)
+    ra.ring_attn_bwd_step(q, k1, v1, do, lse2, delta, dq2, dk2b, dv2b, init_dkv=True, scale=D ** -0.5, causal=True,
+                          q_off=[Nk - Nq], k_off=[h])
+    torch.cuda.synchronize()
+    assert (dq1 - dq2).abs().max().item() <= 1e-5 * max(dq1.abs().max().item(), 1e-6)
+    for half, whole in ((torch.cat([dk2a, dk2b], dim=2), dk1), (torch.cat([dv2a, dv2b], dim=2), dv1)):
+        assert torch.equal(half, whole)  # the same rows, summed in the same order
+    qf, kf, vf, dof = (x[0].cpu().numpy().astype(np.float64) for x in (q, k, v, do))
+    rq, rk, rv = oracle.attention_backward_reference(qf, kf, vf, dof, causal=True, q_pos=np.arange(Nq) + Nk - Nq,
+                                                     k_pos=np.arange(Nk))
+    for name, got, ref in (("dq", dq1, rq), ("dk", dk1, rk), ("dv", dv1, rv)):
+        emax, efro = _errors(got[0].cpu().numpy(), ref)
+        print(f"[bwd] step fp32 D={D} {name}: max {emax:.2e} fro {efro:.2e}", flush=True)
+        assert emax <= TOL_F32_MAX and efro <= TOL_F32_FRO, name

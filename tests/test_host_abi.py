@@ -201,8 +201,9 @@ def _bwd_step(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(dk=None), -1), (dict(n_dev=0), -1), (dict(Hq=3, Hkv=2), -1), (dict(flags=4), -1),
-    (dict(scale=-1.0), -1), (dict(mask=1), -1), (dict(D=64), -2), (dict(dtype=0), -2), (dict(D=129), -2),
+    (dict(scale=-1.0), -1), (dict(mask=1), -1), (dict(dtype=7), -1), (dict(D=129), -2),
     (dict(dq=FAKE), -1),            # dq aliases q
+    (dict(dtype=0, dq=FAKE + 2048), -1),  # fp32 q spans 4096 bytes: dq starts inside it
     (dict(dv=FAKE * 8 + 64), -1),   # dv overlaps dk
     (dict(Nq=0, Nk=0), 0),          # nothing to do
 ])
@@ -232,7 +233,7 @@ def test_bwd_prep_and_local_reject_bad_arguments():
                                      a["dtype"], a["scale"], a["mask"], a["layout"], a["ws"], a["ws_bytes"], None, None)
     assert call(ws_bytes=ws - 1) == -4
     assert call(layout=2, n=7) == -1    # zigzag needs n even
-    assert call(D=64) == -2 and call(dtype=0) == -2
+    assert call(D=129) == -2 and call(dtype=7) == -1
     assert call(layout=3) == -1 and call(dev0=4) == -1 and call(dk=None) == -1
     assert call(dq=FAKE) == -1          # dq aliases q
     assert call(ws=FAKE * 8) == -1      # workspace aliases k
