@@ -189,6 +189,8 @@ def test_bwd_step_accumulates_and_splits(gpu_lib):
     ("f32", 16, False, "contiguous", 33, 1, 2),
     ("bf16", 64, False, "contiguous", 96, 0, None),
     ("bf16", 80, True, "zigzag", 70, 1, 2),
+    ("f32", 3, True, "striped", 21, 0, None),     # odd head dim: lanes past D idle
+    ("bf16", 1, False, "contiguous", 17, 2, 2),   # head dim 1
 ])
 def test_bwd_ring_generic_kernels(gpu_lib, dtype, D, causal, layout, n, dev0, n_local):
     """Every (dtype, head dim) other than bf16 at 128 runs the plain fp32 kernel pair."""
