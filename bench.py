@@ -317,6 +317,17 @@ def run_ffn_workload(w, measure_clock=True):
 
 
 def sample_sclk(call, torch, ms_per_call, seconds=1.2):
+    """sample_clock_once, repeated once over a longer window when the first median is implausibly low
+    for a GPU kept busy (below 1300 MHz: a stale reading; under sustained MFMA load this part has
+    read 1.7-2.3 GHz), so that one bad reading does not inflate the at-clock fractions."""
+    sclk, busy = sample_clock_once(call, torch, ms_per_call, seconds)
+    if sclk is not None and busy is not None and busy >= 0.9 and sclk < 1300:
+        log(f"clock reading {sclk:.0f} MHz under load looks stale; sampling again")
+        sclk, busy = sample_clock_once(call, torch, ms_per_call, 2 * seconds)
+    return sclk, busy
+
+
+def sample_clock_once(call, torch, ms_per_call, seconds):
     """(median GFX clock in MHz, GPU busy fraction) while the same calls keep the GPU busy: a
     background thread reads amdsmi every 10 ms while this thread keeps enqueuing calls for
     `seconds`; the first third of the readings is dropped (the reading lags).  The busy fraction is
