@@ -11,11 +11,13 @@ What is here, in float64 NumPy:
   result, so it is the oracle for every GPU parity test.
 * :func:`attention_rows` — the same definition evaluated only on chosen (batch, head, token) rows,
   for workloads too large for the full O(S^2) computation.
-* :func:`ring_replay` — the ring schedule with the online-softmax fold, in the pages' order and
-  notation, used to check the method's own claims (exactness, arrival-order invariance) on the CPU.
-* :func:`attention_backward_reference`, :func:`attention_backward_rows` — the gradients dQ, dK, dV
-  of the same definition for an output gradient dO (chain rule written out; the pages use the ring
-  for training but do not spell out its backward pass).
+* :func:`ring_replay`, :func:`ring_schedule` — the ring schedule and the online-softmax fold of each
+  device's running state, used to check the method's own claims (exactness, arrival-order
+  invariance) on the CPU.
+* :func:`attention_backward_reference`, :func:`attention_backward_rows`,
+  :func:`attention_backward_key_rows` — the gradients dQ, dK, dV of the same definition for an output
+  gradient dO (chain rule written out; the pages use the ring for training but do not spell out its
+  backward pass), in full, for chosen query rows, or for chosen key rows.
 * :func:`ffn_reference`, :func:`gelu`, :func:`relu` — the position-wise feed-forward that the blockwise
   method computes after attention, y = act(x W1 + b1) W2 + b2.
 * :mod:`oracle.layout` — contiguous, striped and zigzag token-to-shard assignment.
@@ -23,13 +25,13 @@ What is here, in float64 NumPy:
 Every function is pinned by CPU tests to facts outside itself (the pages' demonstration, library
 routines, closed forms, brute force); none is "parity unpinned".
 """
-from .attention import attention_reference, attention_rows, ring_replay
-from .backward import attention_backward_reference, attention_backward_rows
+from .attention import attention_reference, attention_rows, ring_replay, ring_schedule
+from .backward import attention_backward_key_rows, attention_backward_reference, attention_backward_rows
 from .ffn import ffn_reference, gelu, relu
 from .layout import shard_positions, striped_permutation, contiguous_permutation, zigzag_permutation
 
 __all__ = [
-    "attention_reference", "attention_rows", "ring_replay",
-    "attention_backward_reference", "attention_backward_rows", "ffn_reference", "gelu", "relu",
+    "attention_reference", "attention_rows", "ring_replay", "ring_schedule",
+    "attention_backward_reference", "attention_backward_rows", "attention_backward_key_rows", "ffn_reference", "gelu", "relu",
     "shard_positions", "striped_permutation", "contiguous_permutation", "zigzag_permutation",
 ]

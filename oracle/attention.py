@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention_reference", "attention_rows", "ring_replay"]
+__all__ = ["attention_reference", "attention_rows", "ring_replay", "ring_schedule"]
 
 
 def _attend(qrows, qpos, kh, vh, kpos, scale, causal):
@@ -123,68 +123,90 @@ def attention_rows(q, k, v, rows, *, scale=None, causal=False, q_pos=None, k_pos
     return out, lse
 
 
+def ring_schedule(N, order=None):
+    """Which key/value block every device holds at every ring step: table[i][step].
+
+    On the ring each device starts with its own block and, after every step, takes over the block
+    its predecessor held, so at step s device i holds block (i - s) mod N (Ultralytics glossary,
+    "Ring Attention", section "Como funciona a atenção em anel").  An explicit ``order`` (one list
+    of N block indices per device) replaces that rotation, for the arrival-order checks.
+    """
+    if order is not None:
+        return [list(map(int, row)) for row in order]
+    return [[(i - s) % N for s in range(N)] for i in range(N)]
+
+
+class _FoldState:
+    """Per-device online-softmax state of a query block: reference exponent m (the running row
+    maximum of the scores folded so far; -inf before any visible key), normaliser l (sum of
+    exp(score - m)) and accumulator acc (sum of exp(score - m) * value)."""
+
+    def __init__(self, n, D, dt):
+        self.m = np.full((n, 1), -np.inf, dtype=dt)
+        self.l = np.zeros((n, 1), dtype=dt)
+        self.acc = np.zeros((n, D), dtype=dt)
+
+
+def _fold_block(st, s, vj, dt, stabilize):
+    """Fold one block's scaled scores s [n, nk] (masked keys at -inf) and values vj into ``st``.
+
+    Stabilised (the running-maximum form of "Sequence Parallelism and Ring Attention", section
+    "Approfondimento tecnico"): the reference moves to the larger of the old maximum and the block's
+    maximum, the old sums are rescaled by exp(m_old - m_new), and the block's terms enter as
+    exp(s - m_new).  A row with no visible key yet keeps the empty state (exp of -inf - -inf is never
+    formed).  Unstabilised: plain exp(s) terms are added, as the demonstration on the Ultralytics page
+    does; m stays 0.
+    """
+    if not stabilize:
+        w = np.exp(s)
+        st.acc = st.acc + w @ vj
+        st.l = st.l + w.sum(axis=1, keepdims=True)
+        st.m = np.zeros_like(st.m)
+        return
+    m_new = np.maximum(st.m, s.max(axis=1, keepdims=True))
+    live = np.isfinite(m_new)
+    ref = np.where(live, m_new, 0)
+    rescale = np.where(live, np.exp(st.m - ref), 1).astype(dt)
+    w = np.where(live, np.exp(s - ref), 0).astype(dt)
+    st.acc = rescale * st.acc + w @ vj
+    st.l = rescale * st.l + w.sum(axis=1, keepdims=True)
+    st.m = m_new
+
+
 def ring_replay(q_blocks, k_blocks, v_blocks, *, scale, causal=False, q_pos_blocks=None, k_pos_blocks=None,
                 order=None, stabilize=True, dtype=np.float64, trace=None):
-    """The ring schedule with the online-softmax fold, one head, on the CPU.
+    """Ring attention of N emulated devices, one head, on the CPU, step by step.
 
-    Device i keeps query block i for the whole computation.  In step ``step`` it holds key/value
-    block ``j = (i - step) mod N`` (the block that arrived from the previous device), or
-    ``order[i][step]`` when an explicit arrival order is given.  It folds that block into a
-    numerator (running sum of exponentiated scores times values) and a denominator (running sum
-    of exponentiated scores); after the last step it divides the two.
+    The schedule comes first (:func:`ring_schedule`); then all devices advance together, one ring
+    step at a time: at each step every device scores its fixed query block against the block it
+    holds, masks keys whose position lies after the query's (when causal), and folds the result into
+    its own state (:func:`_fold_block`).  Once every step has run, each device divides accumulator by
+    normaliser; its log-sum-exp is m + log(l).
 
-    With ``stabilize`` the fold keeps a running row maximum m and, when a block raises it, rescales
-    the earlier numerator and denominator by exp(m_old - m_new) before adding the new block's
-    exp(s - m_new) terms.  Without it the plain exp(s) of the pages' demonstration is summed.
-
-    Causal masking (when enabled) removes key positions greater than the query position.  A row
-    whose running maximum is still -inf (nothing visible so far) keeps a zero state: exp of
-    (-inf) - (-inf) is never formed.
-
-    Blocks are 2-D arrays [n, D].  Returns (outputs, lses): lists with one [n, D] and one [n]
-    array per device, in ``dtype``.  If ``trace`` is a list, the block index held by each device
-    at each step is appended to it as ``trace[i][step]``.
+    Blocks are 2-D arrays [n, D] (positions per block in q_pos_blocks / k_pos_blocks when causal).
+    Returns (outputs, lses): per device one [n, D] and one [n] array in ``dtype``.  If ``trace`` is a
+    list, each device's row of the schedule is appended to it.
     """
     N = len(q_blocks)
     dt = np.dtype(dtype)
-    outputs, lses = [], []
-    for i in range(N):
-        qi = np.asarray(q_blocks[i], dtype=dt)
-        n, D = qi.shape
-        numerator = np.zeros((n, D), dtype=dt)
-        denominator = np.zeros((n, 1), dtype=dt)
-        m = np.full((n, 1), -np.inf, dtype=dt)
-        held = []
-        for step in range(N):
-            j = (i - step) % N if order is None else order[i][step]
-            held.append(j)
-            kj = np.asarray(k_blocks[j], dtype=dt)
-            vj = np.asarray(v_blocks[j], dtype=dt)
-            s = (qi @ kj.T) * dt.type(scale)
+    table = ring_schedule(N, order)
+    qs = [np.asarray(b, dtype=dt) for b in q_blocks]
+    states = [_FoldState(qb.shape[0], qb.shape[1], dt) for qb in qs]
+    for step in range(N):
+        for i in range(N):
+            j = table[i][step]
+            s = (qs[i] @ np.asarray(k_blocks[j], dtype=dt).T) * dt.type(scale)
             if causal:
-                visible = np.asarray(k_pos_blocks[j])[None, :] <= np.asarray(q_pos_blocks[i])[:, None]
-                s = np.where(visible, s, dt.type(-np.inf))
-            if stabilize:
-                m_new = np.maximum(m, s.max(axis=1, keepdims=True))
-                seen = np.isfinite(m_new)                 # rows with at least one visible key so far
-                m_ref = np.where(seen, m_new, 0)          # never form (-inf) - (-inf)
-                alpha = np.where(seen, np.exp(m - m_ref), 1).astype(dt)
-                p = np.where(seen, np.exp(s - m_ref), 0).astype(dt)
-                numerator = alpha * numerator + p @ vj
-                denominator = alpha * denominator + p.sum(axis=1, keepdims=True)
-                m = m_new
-            else:
-                p = np.exp(s)
-                numerator = numerator + p @ vj
-                denominator = denominator + p.sum(axis=1, keepdims=True)
+                later = np.asarray(k_pos_blocks[j])[None, :] > np.asarray(q_pos_blocks[i])[:, None]
+                s = np.where(later, dt.type(-np.inf), s)
+            _fold_block(states[i], s, np.asarray(v_blocks[j], dtype=dt), dt, stabilize)
+    outputs, lses = [], []
+    for st in states:
         with np.errstate(divide="ignore", invalid="ignore"):
-            out = np.where(denominator > 0, numerator / denominator, 0).astype(dt)
-            if stabilize:
-                lse = np.where(denominator[:, 0] > 0, m[:, 0] + np.log(denominator[:, 0]), -np.inf)
-            else:
-                lse = np.log(denominator[:, 0])
+            out = np.where(st.l > 0, st.acc / st.l, 0).astype(dt)
+            lse = np.where(st.l[:, 0] > 0, st.m[:, 0] + np.log(st.l[:, 0]), -np.inf)
         outputs.append(out)
         lses.append(lse.astype(dt))
-        if trace is not None:
-            trace.append(held)
+    if trace is not None:
+        trace.extend(table)
     return outputs, lses

@@ -21,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention_backward_reference", "attention_backward_rows"]
+__all__ = ["attention_backward_reference", "attention_backward_rows", "attention_backward_key_rows"]
 
 
 def _row_grads(qrows, qpos, kh, vh, kpos, do_rows, scale, causal):
@@ -103,3 +103,58 @@ def attention_backward_rows(q, k, v, do, rows, *, scale=None, causal=False, q_po
                                   do[b, t, h, :].astype(np.float64), scale, causal)
             out[sel] = dq
     return out
+
+
+def attention_backward_key_rows(q, k, v, do, rows, *, scale=None, causal=False, q_pos=None, k_pos=None, row_chunk=256):
+    """dk and dv of selected key rows only: rows int [R, 3] of (batch, key/value head, key index).
+
+    A key's gradients sum over every query row of every query head in its group that sees it, and each
+    term needs that query's softmax weight p_tu = exp(s_tu - lse_t) and delta_t = sum_w p_tw dp_tw =
+    <dO_t, o_t>; so for each (batch, key/value head) the forward of the definition is evaluated first
+    for the query rows that can see a selected key (log-sum-exp and output over all their visible keys),
+    then, with ds_tu = p_tu (dp_tu - delta_t) and dp_tu = <dO_t, v_u>:
+        dk_u = scale * sum_t ds_tu q_t,   dv_u = sum_t p_tu dO_t.
+    Returns (dk [R, D], dv [R, D]) float64 in the order of ``rows``.
+    """
+    q, k, v, do, scale, g = _prep(q, k, v, do, scale)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    Sq, Sk, D = q.shape[1], k.shape[1], q.shape[3]
+    qpos = np.arange(Sq) if q_pos is None else np.asarray(q_pos)
+    kpos = np.arange(Sk) if k_pos is None else np.asarray(k_pos)
+    dk = np.zeros((len(rows), D))
+    dv = np.zeros((len(rows), D))
+    keys = rows[:, 0] * k.shape[2] + rows[:, 1]
+    for key in np.unique(keys):
+        idx = np.nonzero(keys == key)[0]
+        b, kvh = int(rows[idx[0], 0]), int(rows[idx[0], 1])
+        kh = k[b, :, kvh, :].astype(np.float64)
+        vh = v[b, :, kvh, :].astype(np.float64)
+        sel = rows[idx, 2]
+        ks, vs, ps = kh[sel], vh[sel], kpos[sel]
+        # queries that see at least one selected key (all of them without a mask)
+        tq = np.nonzero(qpos >= ps.min())[0] if causal else np.arange(Sq)
+        for h in range(kvh * g, (kvh + 1) * g):
+            for c0 in range(0, len(tq), row_chunk):
+                t = tq[c0:c0 + row_chunk]
+                qt = q[b, t, h, :].astype(np.float64)
+                dot = do[b, t, h, :].astype(np.float64)
+                # forward over every key the rows see: log-sum-exp and output
+                s_all = (qt @ kh.T) * scale
+                if causal:
+                    s_all = np.where(kpos[None, :] <= qpos[t][:, None], s_all, -np.inf)
+                mx = s_all.max(axis=1, keepdims=True)
+                e = np.exp(s_all - mx)
+                den = e.sum(axis=1, keepdims=True)
+                lse = mx + np.log(den)
+                out = (e @ vh) / den
+                delta = (dot * out).sum(axis=1, keepdims=True)
+                # the selected keys' terms
+                s_sel = (qt @ ks.T) * scale
+                if causal:
+                    s_sel = np.where(ps[None, :] <= qpos[t][:, None], s_sel, -np.inf)
+                p = np.exp(s_sel - lse)                  # 0 where masked
+                dp = dot @ vs.T
+                ds = p * (dp - delta)
+                dk[idx] += scale * (ds.T @ qt)
+                dv[idx] += p.T @ dot
+    return dk, dv

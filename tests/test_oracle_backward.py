@@ -114,3 +114,36 @@ def test_backward_rows_equal_full():
     got = oracle.attention_backward_rows(q, k, v, do, rows, causal=True)
     want = np.stack([dq[b, t, h] for b, h, t in rows])
     assert np.abs(got - want).max() < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_rows_match_torch_autograd(causal):
+    """dK and dV of chosen key rows (grouped-query heads, two batch elements, positions with an
+    interleaved map, rows that see nothing) against torch autograd of the softmax formula."""
+    B, S, Hq, Hkv, D = 2, 19, 6, 2, 8
+    q, k, v, do = _rand((B, S, Hq, D), 51), _rand((B, S, Hkv, D), 52), _rand((B, S, Hkv, D), 53), _rand((B, S, Hq, D), 54)
+    qpos = np.arange(S) * 2 + 1
+    kpos = np.arange(S) * 2 + (4 if causal else 0)
+    rows = np.array([[b, h, u] for b in range(B) for h in range(Hkv) for u in range(S)])[::3]
+    dk, dv = oracle.attention_backward_key_rows(q, k, v, do, rows, scale=0.37, causal=causal, q_pos=qpos, k_pos=kpos)
+    if causal:
+        # query rows 0 and 1 see no key: leave them out of autograd (their softmax rows are all -inf there)
+        _, tk, tv = _torch_grads(q[:, 2:], k, v, do[:, 2:], 0.37, True, qpos[2:], kpos)
+    else:
+        _, tk, tv = _torch_grads(q, k, v, do, 0.37, False, qpos, kpos)
+    want_k = np.stack([tk[b, u, h] for b, h, u in rows])
+    want_v = np.stack([tv[b, u, h] for b, h, u in rows])
+    assert np.abs(dk - want_k).max() < 1e-12 and np.abs(dv - want_v).max() < 1e-12
+
+
+def test_backward_key_rows_equal_full_and_catch_a_wrong_head_map():
+    q, k, v, do = _rand((1, 24, 4, 8), 61), _rand((1, 24, 2, 8), 62), _rand((1, 24, 2, 8), 63), _rand((1, 24, 4, 8), 64)
+    _, dk, dv = oracle.attention_backward_reference(q, k, v, do, causal=True)
+    rows = np.array([[0, 0, 0], [0, 1, 23], [0, 1, 5], [0, 0, 17]])
+    gk, gv = oracle.attention_backward_key_rows(q, k, v, do, rows, causal=True)
+    assert np.abs(gk - np.stack([dk[b, u, h] for b, h, u in rows])).max() < 1e-13
+    assert np.abs(gv - np.stack([dv[b, u, h] for b, h, u in rows])).max() < 1e-13
+    # swapping the two key/value heads' query groups changes the answer
+    q_swapped = q[:, :, [2, 3, 0, 1]]
+    bk, _ = oracle.attention_backward_key_rows(q_swapped, k, v, do, rows, causal=True)
+    assert np.abs(bk - gk).max() > 1e-3
