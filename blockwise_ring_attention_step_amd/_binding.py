@@ -28,6 +28,7 @@ RA_STEP_INIT = 1
 RA_BWD_INIT_DQ, RA_BWD_INIT_DKV = 1, 2
 RA_MAX_DEV, RA_MAX_D = 64, 128
 RA_FFN_GELU, RA_FFN_RELU = 0, 1
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE, RA_ERR_INJECTED = 0, -1, -2, -3, -4, -5
 _ACTIVATIONS = {"gelu": RA_FFN_GELU, "relu": RA_FFN_RELU}
 
 EXPORTED_SYMBOLS = (

@@ -10,6 +10,8 @@
 // the first devices that the Ultralytics page attributes to causal masking.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "internal.h"
@@ -214,6 +216,42 @@ bool misaligned(std::initializer_list<const void*> ps, uintptr_t align) {
   return false;
 }
 
+// Test hooks of the ring drivers, read from the environment at every call (documented in
+// ring_attn.h): RING_ATTN_HOP_STRESS = comma-separated "poison", "jitter-copy", "jitter-compute";
+// RING_ATTN_FAIL_AT_STEP = k (ring_attn_local stops before step k).
+struct HopStress {
+  bool poison = false;          // NaN-fill every receive-slot range just before it is written
+  bool jitter_copy = false;     // a bounded sleep kernel before each step's hop copies
+  bool jitter_compute = false;  // a bounded sleep kernel before each step kernel
+  int fail_at = -1;             // stop before this step (-1: run the whole ring)
+};
+
+HopStress read_hop_stress() {
+  HopStress h;
+  if (const char* e = std::getenv("RING_ATTN_HOP_STRESS")) {
+    const std::string v(e);
+    h.poison = v.find("poison") != std::string::npos;
+    h.jitter_copy = v.find("jitter-copy") != std::string::npos;
+    h.jitter_compute = v.find("jitter-compute") != std::string::npos;
+  }
+  if (const char* e = std::getenv("RING_ATTN_FAIL_AT_STEP")) {
+    char* end = nullptr;
+    const long k = std::strtol(e, &end, 10);
+    if (end != e && k >= 0 && k < (1L << 30)) h.fail_at = (int)k;
+  }
+  return h;
+}
+
+constexpr unsigned kJitterRounds = 48;  // ~0.2 ms of sleep per jitter kernel at 2 GHz
+constexpr uint16_t kPoison = 0xFFFF;    // NaN as bf16 and, in pairs, as fp32
+
+// NaN-fill `bytes` (a whole number of 16-bit words) at p on `stream` when poisoning.
+hipError_t poison(const HopStress& hs, void* p, size_t bytes, hipStream_t stream) {
+  return hs.poison ? ra::launch_fill_u16(p, bytes / 2, kPoison, stream) : hipSuccess;
+}
+
+hipError_t jitter(bool on, hipStream_t stream) { return on ? ra::launch_spin(kJitterRounds, stream) : hipSuccess; }
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +263,7 @@ const char* ring_attn_strerror(int code) {
     case RA_ERR_UNSUPPORTED: return "unsupported configuration";
     case RA_ERR_HIP: return "HIP runtime error";
     case RA_ERR_WORKSPACE: return "workspace too small";
+    case RA_ERR_INJECTED: return "stopped by RING_ATTN_FAIL_AT_STEP";
     default: return "unknown status";
   }
 }
@@ -403,6 +442,8 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   hipStream_t xs = (hipStream_t)copy_stream;
   const bool causal = mask == RA_MASK_CAUSAL;
   const int64_t st = layout_stride(layout, P);
+  const HopStress hs = read_hop_stress();
+  const int stop = hs.fail_at >= 0 && hs.fail_at < P ? hs.fail_at : P;  // steps run: [0, stop)
 
   // per-unit schedule (a unit is a device's whole query block, or one of its two zigzag chunks):
   // class of every (step, unit) and each unit's first and last computed step
@@ -498,6 +539,8 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
       // every device receives block (i - s) mod P from the source (pinned host memory here)
       for (int t = 0; t < n_local; ++t) {
         const int j = ((dev0 + t - s) % P + P) % P;
+        if ((e = poison(hs, stage_k[sl] + t * blk, blk, xs)) != hipSuccess) return e;
+        if ((e = poison(hs, stage_v[sl] + t * blk, blk, xs)) != hipSuccess) return e;
         if ((e = hipMemcpyAsync(stage_k[sl] + t * blk, ksrc + j * blk, blk, kind, xs)) != hipSuccess) return e;
         if ((e = hipMemcpyAsync(stage_v[sl] + t * blk, vsrc + j * blk, blk, kind, xs)) != hipSuccess) return e;
       }
@@ -517,6 +560,8 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
              hop_src(s, t2, vsrc, stage_v) == v0 + (size_t)(t2 - t) * blk)
         ++t2;
       const size_t bytes = (size_t)(t2 - t) * blk;
+      if ((e = poison(hs, stage_k[sl] + t * blk, bytes, xs)) != hipSuccess) return e;
+      if ((e = poison(hs, stage_v[sl] + t * blk, bytes, xs)) != hipSuccess) return e;
       if ((e = hipMemcpyAsync(stage_k[sl] + t * blk, k0, bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
       if ((e = hipMemcpyAsync(stage_v[sl] + t * blk, v0, bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
       t = t2;
@@ -524,15 +569,17 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
     return hipSuccess;
   };
 
-  if (kv_src_is_host) {
+  if (kv_src_is_host && stop > 0) {
+    RA_CHECK(jitter(hs.jitter_copy, xs));
     RA_CHECK(enqueue_hop(0));
     RA_CHECK(hipEventRecord(ev_copy[0], xs));
   }
-  for (int s = 0; s < P; ++s) {
+  for (int s = 0; s < stop; ++s) {
     // copies for step s+1, into the slot that step s-1 read; they may read blocks that kernel s-1
     // handed over, so they wait for it
-    if (needs_copy(s + 1)) {
+    if (s + 1 < stop && needs_copy(s + 1)) {
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
+      RA_CHECK(jitter(hs.jitter_copy, xs));
       RA_CHECK(enqueue_hop(s + 1));
       RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
     }
@@ -579,16 +626,40 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
         p.k_off[x] = un.k_off;
         p.q_stride = un.stride;  // the same for every unit of a layout
         p.k_stride = un.stride;
-        p.dflags[x] = (s == first_step[u] ? ra::kDevInit : 0) | (s == last_step[u] ? ra::kDevFinal : 0);
+        p.dflags[x] = (s == first_step[u] ? ra::kDevInit : 0) |
+                      (s == last_step[u] && stop == P ? ra::kDevFinal : 0);
         const int succ = in_step_hop ? fwd_to[(size_t)s * n_local + t] : -1;
         p.fwd_k[x] = succ >= 0 ? (void*)(stage_k[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
         p.fwd_v[x] = succ >= 0 ? (void*)(stage_v[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+        if (succ >= 0) {  // the slot this kernel fills was last read by step s-1, earlier on this stream
+          RA_CHECK(poison(hs, p.fwd_k[x], blk, cs));
+          RA_CHECK(poison(hs, p.fwd_v[x], blk, cs));
+        }
       }
+      RA_CHECK(jitter(hs.jitter_compute, cs));
       hipEvent_t e0 = step_events && ch == 0 ? (hipEvent_t)step_events[2 * s] : nullptr;
       hipEvent_t e1 = step_events && ch + 1 == n_chunks ? (hipEvent_t)step_events[2 * s + 1] : nullptr;
       RA_CHECK(launch_step(p, dtype, cs, e0, e1));
     }
-    if (needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+    if (s + 2 < stop && needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+  }
+  if (stop < P) {
+    // stopped before step `stop`: the workspace state is the fold of steps [0, stop); devices that
+    // have not computed yet get the empty state so that every device's state is a valid checkpoint
+    // (a zigzag unit computes at step 0, so only stop == 0 leaves zigzag devices untouched)
+    for (int t = 0; t < n_local; ++t)
+      if (stop == 0 || (nh == 1 && (first_step[t] < 0 || first_step[t] >= stop))) {
+        int slot_t = t;
+        RA_CHECK(ra::launch_init_state(o_acc, m_st, l_st, n_local, &slot_t, 1, B, Hq, n, D, cs));
+      }
+    if (two_streams) {
+      RA_CHECK(hipEventRecord(ev_copy[0], xs));
+      RA_CHECK(hipStreamWaitEvent(cs, ev_copy[0], 0));
+      RA_CHECK(hipEventRecord(ev_comp[0], cs));
+      RA_CHECK(hipStreamWaitEvent(xs, ev_comp[0], 0));
+    }
+    cleanup();
+    return RA_ERR_INJECTED;
   }
   // devices that never computed (no visible block): empty output (a zigzag unit always computes:
   // its own block holds keys at or before each of its queries)
@@ -771,7 +842,7 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   hipStream_t cs = (hipStream_t)compute_stream;
   hipStream_t xs = (hipStream_t)copy_stream;
   const bool causal = mask == RA_MASK_CAUSAL;
-  const int64_t st = layout_stride(layout, P);
+  const HopStress hs = read_hop_stress();
 
   // schedule over units (a device's whole query block, or one of its two zigzag chunks, as in the
   // forward): class of every (step, unit), the first computed step of each unit's query gradient and
@@ -838,7 +909,10 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
       int t2 = t + 1;
       while (t2 < n_local && ((dev0 + t2 - s) % P + P) % P == j0 + (t2 - t)) ++t2;  // contiguous source run
       const size_t bytes = (size_t)(t2 - t) * blk;
-      hipError_t e = hipMemcpyAsync(stage_k[sl] + t * blk, ksrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
+      hipError_t e = poison(hs, stage_k[sl] + t * blk, bytes, xs);
+      if (e == hipSuccess) e = poison(hs, stage_v[sl] + t * blk, bytes, xs);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(stage_k[sl] + t * blk, ksrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
       if (e == hipSuccess)
         e = hipMemcpyAsync(stage_v[sl] + t * blk, vsrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
       if (e != hipSuccess) return e;
@@ -855,6 +929,7 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   for (int s = 0; s < P; ++s) {
     if (s + 1 < P) {  // copies for step s+1, into the slot that step s-1 read
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
+      RA_CHECK(jitter(hs.jitter_copy, xs));
       RA_CHECK(enqueue_hop(s + 1));
       RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
     }
@@ -909,6 +984,7 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
       }
       return hipSuccess;
     };
+    RA_CHECK(jitter(hs.jitter_compute, cs));
     RA_CHECK(launch_units(-1, true));
     if (nh == 1) {
       RA_CHECK(launch_units(-1, false));

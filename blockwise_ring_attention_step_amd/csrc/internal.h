@@ -124,6 +124,10 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
 hipError_t launch_ffn_gemm_bf16(const FfnGemmParams& p, int act, hipStream_t stream);
 hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, void* o, float* lse, int n_dev,
                            int B, int Hq, int Nq, int D, int out_dtype, hipStream_t stream);
+// Test hooks of the ring drivers: every 16-bit word of [p, p + 2 n_words) set to `value`; one wave
+// that sleeps `rounds` x 8128 clocks (bounded) and exits.
+hipError_t launch_fill_u16(void* p, size_t n_words, uint16_t value, hipStream_t stream);
+hipError_t launch_spin(unsigned rounds, hipStream_t stream);
 hipError_t launch_init_state(float* o_acc, float* m, float* l, int n_dev_total, const int* slots, int n_slots,
                              int B, int Hq, int Nq, int D, hipStream_t stream);
 

@@ -11,6 +11,8 @@
 // 256-thread workgroup; the dot product is reduced across the 16 lanes with xor shuffles.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace ra {
@@ -169,7 +171,30 @@ __global__ __launch_bounds__(256) void init_state_kernel(float* o_acc, float* m,
   if (i < rows * D) o_acc[base * D + i] = 0.f;
 }
 
+// Every 16-bit word of [p, p + n) set to `value` (grid-stride loop).
+__global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t* __restrict__ p, size_t n, uint16_t value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// One wave that sleeps for `rounds` rounds of the longest s_sleep (64 x 127 clocks each) and exits.
+__global__ __launch_bounds__(64) void spin_kernel(unsigned rounds) {
+  for (unsigned r = 0; r < rounds; ++r) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace
+
+hipError_t launch_fill_u16(void* p, size_t n_words, uint16_t value, hipStream_t stream) {
+  if (n_words == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n_words + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint16_t*)p, n_words, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_spin(unsigned rounds, hipStream_t stream) {
+  hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, stream, rounds);
+  return hipGetLastError();
+}
 
 hipError_t launch_step_generic(const StepParams& p, int dtype, hipStream_t stream, hipEvent_t ev_start,
                                hipEvent_t ev_stop) {

@@ -39,12 +39,23 @@
  *     Ukufana Nokunakwa Kwendandatho") is two such runs per shard; the driver handles it.
  *   - Grouped-query attention: query head h reads key/value head h / (Hq / Hkv).
  *
- * Running state between ring steps (fp32, caller-owned, persistent across calls):
+ * Running state between ring steps (fp32, caller-owned, persistent across calls): the running
+ * maximum and normaliser of "Sequence Parallelism and Ring Attention", section "Approfondimento
+ * tecnico", kept in base 2:
  *   o_acc[dev, b, h, t, :] = sum_u 2^(x_u - m[dev,b,h,t]) * v_u
  *   l[dev, b, h, t]        = sum_u 2^(x_u - m[dev,b,h,t])
- *   where x_u = log2(e) * scale * <q_t, k_u> over the visible keys folded so far, and m is a
- *   reference exponent (the running maximum of x, possibly lagging it by at most 8), or -inf while
- *   no visible key has been folded (then o_acc = 0 and l = 0).
+ *   where x_u = log2(e) * scale * <q_t, k_u> over the visible keys folded so far (N of them) and
+ *   m is a reference exponent, or -inf while no visible key has been folded (then o_acc = 0 and
+ *   l = 0).  The quotient o_acc / l and the log-sum-exp (m + log2 l) * ln 2 do not depend on which
+ *   reference is used, so m need not be the running maximum X = max_u x_u.  Bounds every state
+ *   written by this library satisfies (up to fp32 rounding of x):
+ *     m <= X <= m + 64         m is the exact maximum of some of the folded scores; the MFMA kernel
+ *                              moves it only when a 64-key tile's partial sum of 2^(x - m) over one
+ *                              lane's 32 keys would pass 2^64 (the generic kernel keeps m = X)
+ *     1 <= l <= N * 2^64       every folded term is at most 2^64, the largest at least 1
+ *     |o_acc| <= l * max_u |v_u| (elementwise over d)
+ *   A state that satisfies these bounds (for example one merged from other states by the same rule:
+ *   m = max(m1, m2), l = 2^(m1 - m) l1 + 2^(m2 - m) l2, likewise o_acc) may be passed back in.
  *   Shapes: o_acc [n_dev, B, Hq, Nq, D], m and l [n_dev, B, Hq, Nq].
  */
 #ifndef RING_ATTN_H
@@ -77,6 +88,7 @@ extern "C" {
 #define RA_ERR_UNSUPPORTED (-2) /* valid but not implemented (e.g. head dim > 128) */
 #define RA_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
 #define RA_ERR_WORKSPACE (-4)   /* workspace too small */
+#define RA_ERR_INJECTED (-5)    /* ring_attn_local stopped early by RING_ATTN_FAIL_AT_STEP (test hook) */
 
 /* ring_attn_step flags */
 #define RA_STEP_INIT 1 /* ignore the incoming state: treat it as m = -inf, l = 0, o_acc = 0 */
@@ -164,17 +176,44 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  * fully masked blocks are still passed on but not computed.  The last step of each device writes
  * o and lse directly.  The call returns after enqueueing; both streams are left ordered after all
  * of its work.
+ *
+ * Workspace layout (R(x) = x rounded up to 256 bytes, blk = B*n*Hkv*D*sizeof(dtype)): K slots 0 and
+ * 1 and V slots 0 and 1 of n_local blocks each (R(n_local*blk) bytes apiece), then the running state
+ * of the local devices as ring_attn_step keeps it: o_acc (R(rows*D*4) bytes), m and l (R(rows*4)
+ * bytes each), rows = n_local*B*Hq*n.
+ *
+ * Test hooks (environment variables read at every call; unset in normal use):
+ *   RING_ATTN_HOP_STRESS  comma-separated: "poison" fills every receive-slot range with NaN on the
+ *                         stream that is about to write it, just before the write (a read of a slot
+ *                         before its block has landed, or a row the in-step hop failed to store,
+ *                         then shows as NaN); "jitter-copy" / "jitter-compute" put a bounded sleep
+ *                         kernel (about 0.2 ms) before each step's hop copies / each step kernel.
+ *                         Results must not change.  ring_attn_bwd_local honours the same three.
+ *   RING_ATTN_FAIL_AT_STEP=k  (0 <= k < P) enqueue steps [0, k) only, without the fused final
+ *                         division, give every local device that has not computed yet the empty
+ *                         state, join the streams and return RA_ERR_INJECTED.  The workspace state is
+ *                         then the ring's checkpoint after k steps: folding the remaining blocks
+ *                         with ring_attn_step and calling ring_attn_finalize completes the ring.
  */
 int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
                     float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
                     float scale, int mask, int layout, void* workspace, size_t workspace_bytes,
                     void* compute_stream, void* copy_stream, void* const* step_events);
 
-/* Workspace size in bytes for ring_attn_local with these arguments (0 on invalid arguments). */
+/* Workspace size in bytes for ring_attn_local with these arguments (0 on invalid arguments): the
+ * device memory one device's share of the ring needs besides its inputs and outputs, namely the two
+ * receive slots of key/value blocks that double-buffer the hop ("Ring Attention Là Gì?",
+ * "Ring Attention Hoạt Động Thế Nào?": the next block arrives while the current one is used) and
+ * the persistent fp32 running state of the local query blocks (Ultralytics "Ring Attention",
+ * "Como funciona a atenção em anel": the accumulated sums each device keeps).  Pure host
+ * arithmetic; no HIP call. */
 size_t ring_attn_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype);
 
 /*
- * ring_attn_plan — the ring schedule as a table, computed on the host (no HIP call).
+ * ring_attn_plan — the ring schedule as a table, computed on the host (no HIP call): the N steps of
+ * Ultralytics "Ring Attention", "Como funciona a atenção em anel" (in step s device i holds the
+ * block its predecessor held one step earlier, i.e. block (i - s) mod P), with the block classes
+ * behind the causal idling that page describes (a fully masked block is not computed).
  * For each step s in [0, P) and each local device i in [dev0, dev0 + n_local), one row of 5 int32:
  *   { s, i, j = (i - s) mod P, staging slot (s mod 2), class }
  * class: 0 = fully masked (skipped), 1 = fully visible, 2 = partially visible (masked tiles).
@@ -283,7 +322,9 @@ int ring_attn_ffn(const void* x, const void* w1, const void* b1, const void* w2,
 /* Workspace size in bytes for ring_attn_ffn with these arguments (0 on invalid arguments). */
 size_t ring_attn_ffn_workspace_bytes(int64_t n_tokens, int d_model, int d_ff, int64_t block_tokens);
 
-/* Human-readable text for a status code (static storage). */
+/* Human-readable text for a status code (static storage; never NULL, "unknown status" for codes
+ * this library does not return).  Not an operation of the method: the pages define no interface, and
+ * this only names the RA_* codes above. */
 const char* ring_attn_strerror(int code);
 
 #ifdef __cplusplus
