@@ -24,3 +24,23 @@ def test_a_distributed_launch_is_refused():
     r = _run(["--steps", "1"], {"WORLD_SIZE": "4"})
     assert r.returncode == 2
     assert "WORLD_SIZE 4" in r.stderr
+
+
+def test_bench_sharding_matches_the_oracle_layouts():
+    """bench.py shards its inputs with its own numpy reshapes; each layout must put token
+    oracle.shard_positions(S, P, layout)[i, r] at shard i, row r, or the timed masks would be wrong."""
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle
+
+    B, H, D = 2, 3, 2
+    for S, P in ((48, 4), (64, 8), (24, 2)):
+        x = np.arange(B * S * H * D, dtype=np.int64).reshape(B, S, H, D)
+        for layout in ("contiguous", "striped", "zigzag"):
+            got = bench.shard_np(x, P, layout)
+            pos = oracle.shard_positions(S, P, layout)
+            want = np.ascontiguousarray(x[:, pos.reshape(-1)].reshape(B, P, S // P, H, D).transpose(1, 0, 2, 3, 4))
+            assert got.shape == want.shape
+            assert np.array_equal(got, want), (S, P, layout)

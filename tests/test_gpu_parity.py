@@ -228,7 +228,9 @@ def test_arrival_order_does_not_matter(gpu_lib, dtype, D):
 
 
 def test_splitting_a_block_gives_the_same_state(gpu_lib):
-    """Folding a block in two halves equals folding it at once (the merge is associative)."""
+    """Folding a block in two parts (a split that is not a tile boundary of the second part) gives
+    attention over the whole block: both the one-call and the two-call states finalize to the oracle's
+    output and log-sum-exp at the bf16 tolerances, and to each other within the same bounds."""
     ra = gpu_lib
     n, Hq, D = 256, 2, 128
     q, k, v = _inputs(1, n, Hq, Hq, D, 900, "bf16")
@@ -245,8 +247,87 @@ def test_splitting_a_block_gives_the_same_state(gpu_lib):
         lse = torch.empty((1, 1, Hq, n), dtype=torch.float32, device="cuda")
         ra.ring_attn_finalize(*st, o, lse)
         outs.append((out_to_f64(o), lse.cpu().numpy()))
-    assert max_err(outs[0][0], outs[1][0]) <= 1e-2
-    assert max_err(outs[0][1], outs[1][1]) <= 1e-5
+    ref_o, ref_lse = oracle.attention_reference(to_float(q, "bf16"), to_float(k, "bf16"), to_float(v, "bf16"))
+    for got_o, got_l in outs:
+        assert max_err(got_o[0], ref_o) <= TOL_BF16_O
+        assert max_err(got_l[0], ref_lse) <= TOL_BF16_LSE
+    assert max_err(outs[0][0], outs[1][0]) <= TOL_BF16_O
+    assert max_err(outs[0][1], outs[1][1]) <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("dtype,D,qscale", [("bf16", 128, 1.0), ("bf16", 128, 30.0), ("f32", 48, 30.0)])
+def test_state_after_steps_keeps_the_documented_bounds(gpu_lib, dtype, D, qscale):
+    """The running state read back after two ring_attn_step calls (a fresh fold, then a continuing one
+    with a merge) satisfies the bounds the C header states, against the exact row maximum X of
+    x = log2(e) * scale * q.k over the visible keys (float64, from the same inputs):
+        m <= X <= m + 64,  1 <= l <= N 2^64,  m + log2 l = log2 sum 2^x  (the LSE in base 2),
+        o_acc / l = attention output,
+    and rows that have seen no key hold m = -inf, l = 0, o_acc = 0.  Queries scaled by 30 give
+    score spreads of hundreds of log2 units, so the MFMA kernel's reference exponent lags X by up to
+    its limit; the plain kernel (fp32) keeps m = X."""
+    ra = gpu_lib
+    n_dev, B, Hq, Hkv, Nq, Nk = 2, 1, 4, 2, 300, 200
+    q, k, v = _inputs(B, n_dev * Nq, Hq, Hkv, D, 950 + D, dtype)
+    _, k2, v2 = _inputs(B, n_dev * Nk, Hq, Hkv, D, 960 + D, dtype)
+    k, v = k[:, :n_dev * Nk], v[:, :n_dev * Nk]
+    if qscale != 1.0:
+        qf = to_float(q, dtype) * qscale
+        q = si.bf16_bits(qf) if dtype == "bf16" else qf.astype(np.float32)
+    qd = q.reshape(B, n_dev, Nq, Hq, D).transpose(1, 0, 2, 3, 4)
+    blocks = [(k.reshape(B, n_dev, Nk, Hkv, D).transpose(1, 0, 2, 3, 4), v.reshape(B, n_dev, Nk, Hkv, D).transpose(1, 0, 2, 3, 4)),
+              (k2.reshape(B, n_dev, Nk, Hkv, D).transpose(1, 0, 2, 3, 4), v2.reshape(B, n_dev, Nk, Hkv, D).transpose(1, 0, 2, 3, 4))]
+    # positions: device t's queries at 1000 t + 2 r; block 0's keys at 1000 t + 250 + 2 u (query rows
+    # below 125 see none of them), block 1's keys at 1000 t + 20 + u (query rows below 10 see none):
+    # rows 0..9 end with the empty state, rows 10..124 are first seen by the continuing step
+    q_off = [1000 * t for t in range(n_dev)]
+    k_offs = [[1000 * t + 250 for t in range(n_dev)], [1000 * t + 20 for t in range(n_dev)]]
+    k_strides = [2, 1]
+    scale = 1.0 / math.sqrt(D)
+    tq = to_device(np.ascontiguousarray(qd), dtype)
+    st = _state(n_dev, B, Hq, Nq, D)
+    ra.ring_attn_step(tq, to_device(np.ascontiguousarray(blocks[0][0]), dtype),
+                      to_device(np.ascontiguousarray(blocks[0][1]), dtype), *st, scale=scale, causal=True, q_off=q_off,
+                      q_stride=2, k_off=k_offs[0], k_stride=k_strides[0], init=True)
+    ra.ring_attn_step(tq, to_device(np.ascontiguousarray(blocks[1][0]), dtype),
+                      to_device(np.ascontiguousarray(blocks[1][1]), dtype), *st, scale=scale, causal=True, q_off=q_off,
+                      q_stride=2, k_off=k_offs[1], k_stride=k_strides[1])
+    torch.cuda.synchronize()
+    o_acc, m, l = (x.cpu().numpy().astype(np.float64) for x in st)
+    log2e = 1.0 / math.log(2.0)
+    g = Hq // Hkv
+    checked_lag = 0.0
+    for t in range(n_dev):
+        qpos = q_off[t] + 2 * np.arange(Nq)
+        kk = np.concatenate([to_float(blocks[b][0][t, 0], dtype) for b in (0, 1)]).astype(np.float64)
+        vv = np.concatenate([to_float(blocks[b][1][t, 0], dtype) for b in (0, 1)]).astype(np.float64)
+        kpos = np.concatenate([k_offs[b][t] + k_strides[b] * np.arange(Nk) for b in (0, 1)])
+        ref_o, ref_lse = oracle.attention_reference(to_float(qd[t], dtype), kk[None], vv[None], causal=True,
+                                                    q_pos=qpos, k_pos=kpos)
+        for h in range(Hq):
+            x = (to_float(qd[t, 0, :, h], dtype).astype(np.float64) @ kk[:, h // g].T) * scale * log2e
+            vis = kpos[None, :] <= qpos[:, None]
+            n_vis = vis.sum(axis=1)
+            X = np.where(vis, x, -np.inf).max(axis=1)
+            mh, lh, oh = m[t, 0, h], l[t, 0, h], o_acc[t, 0, h]
+            seen = n_vis > 0
+            assert (~seen).sum() == 10
+            if dtype == "bf16":
+                tol_o, tol_l = TOL_BF16_O, TOL_BF16_LSE
+            else:  # fp32: each x carries about sqrt(D) roundings of its size (see the large-score test)
+                score_err = math.sqrt(D) * 2.0 ** -23 * np.abs(x[vis]).max() / log2e
+                tol_o = TOL_F32 + 2 * score_err * np.abs(vv).max()
+                tol_l = TOL_F32 + 2 * score_err
+            assert np.all(np.isneginf(mh[~seen])) and np.all(lh[~seen] == 0) and np.all(oh[~seen] == 0)
+            eps = 1e-3 + 1e-6 * np.abs(X[seen])
+            assert np.all(mh[seen] <= X[seen] + eps), "reference exponent above the row maximum"
+            assert np.all(X[seen] <= mh[seen] + 64 + eps), "reference exponent lags by more than 64"
+            assert np.all(lh[seen] >= 1 - 1e-4) and np.all(lh[seen] <= n_vis[seen] * 2.0 ** 64 * (1 + 1e-6))
+            assert max_err(mh[seen] + np.log2(lh[seen]), ref_lse[0, h, seen] * log2e) <= tol_l * log2e
+            assert max_err(oh[seen] / lh[seen][:, None], ref_o[0, seen, h]) <= tol_o
+            if dtype == "f32":
+                assert np.all(np.abs(mh[seen] - X[seen]) <= eps)
+            checked_lag = max(checked_lag, float((X[seen] - mh[seen]).max()))
+    print(f"[state] {dtype} D={D} q x{qscale}: largest lag X - m = {checked_lag:.3g} (log2 units)", flush=True)
 
 
 def test_state_snapshot_and_resume(gpu_lib):
