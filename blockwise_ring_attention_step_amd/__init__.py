@@ -12,4 +12,5 @@ from ._binding import (  # noqa: F401
     ring_attn_bwd_prep, ring_attn_bwd_step, ring_attn_bwd_local, ring_attn_bwd_local_workspace_bytes,
     RA_FFN_GELU, RA_FFN_RELU, ring_attn_ffn, ring_attn_ffn_workspace_bytes,
     EXPORTED_SYMBOLS, RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE, RA_ERR_INJECTED,
+    RA_ERR_SCRATCH, ring_attn_local_noalloc, ring_attn_noalloc_scratch_bytes,
 )

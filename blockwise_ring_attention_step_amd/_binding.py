@@ -29,13 +29,14 @@ RA_BWD_INIT_DQ, RA_BWD_INIT_DKV = 1, 2
 RA_MAX_DEV, RA_MAX_D = 64, 128
 RA_FFN_GELU, RA_FFN_RELU = 0, 1
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE, RA_ERR_INJECTED = 0, -1, -2, -3, -4, -5
+RA_ERR_SCRATCH = -6
 _ACTIVATIONS = {"gelu": RA_FFN_GELU, "relu": RA_FFN_RELU}
 
 EXPORTED_SYMBOLS = (
     "ring_attn_step", "ring_attn_finalize", "ring_attn_local", "ring_attn_local_workspace_bytes",
     "ring_attn_plan", "ring_attn_visible_pairs", "ring_attn_strerror",
     "ring_attn_bwd_prep", "ring_attn_bwd_step", "ring_attn_bwd_local", "ring_attn_bwd_local_workspace_bytes",
-    "ring_attn_ffn", "ring_attn_ffn_workspace_bytes",
+    "ring_attn_ffn", "ring_attn_ffn_workspace_bytes", "ring_attn_local_noalloc", "ring_attn_noalloc_scratch_bytes",
 )
 
 _lib = None
@@ -69,6 +70,11 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_local.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                   vp, sz, vp, vp, vp]
     L.ring_attn_local.restype = i32
+    L.ring_attn_local_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                          i32, i32, vp, vp, vp]
+    L.ring_attn_local_noalloc.restype = i32
+    L.ring_attn_noalloc_scratch_bytes.argtypes = []
+    L.ring_attn_noalloc_scratch_bytes.restype = sz
     L.ring_attn_local_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     L.ring_attn_local_workspace_bytes.restype = sz
     L.ring_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32)]
@@ -197,6 +203,35 @@ def ring_attn_local(q_local, k_src, v_src, o, lse, workspace, *, P, dev0, scale,
                                _layout_code(layout, striped), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), cs, xs, ev)
     _check("ring_attn_local", rc)
+
+
+def ring_attn_noalloc_scratch_bytes() -> int:
+    return int(lib().ring_attn_noalloc_scratch_bytes())
+
+
+def ring_attn_local_noalloc(q_local, k_src, v_src, o, lse, *, P, dev0, scale, causal=False, layout=None,
+                            compute_stream=None, copy_stream=None, step_events=None):
+    """ring_attn_local working in the library's fixed device scratch instead of a workspace tensor
+    (allocates no device memory).  Same arguments as ring_attn_local without ``workspace``."""
+    n_local, B, n, Hq, D = q_local.shape
+    Hkv = k_src.shape[3]
+    host_src = not k_src.is_cuda
+    if host_src and not (k_src.is_pinned() and v_src.is_pinned()):
+        raise ValueError("host key/value sources must be pinned")
+    kp = k_src.data_ptr() if host_src else _ptr(k_src)
+    vp = v_src.data_ptr() if host_src else _ptr(v_src)
+    ev = None
+    if step_events is not None:
+        if len(step_events) != 2 * P:
+            raise ValueError("step_events needs 2*P events")
+        ev = (ctypes.c_void_p * (2 * P))(*[e.handle for e in step_events])
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    rc = lib().ring_attn_local_noalloc(_ptr(q_local), kp, vp, 1 if host_src else 0, _ptr(o), _ptr(lse), P, dev0,
+                                       n_local, B, Hq, Hkv, n, D, _dtype_code(q_local), float(scale),
+                                       RA_MASK_CAUSAL if causal else RA_MASK_NONE, _layout_code(layout, False), cs, xs,
+                                       ev)
+    _check("ring_attn_local_noalloc", rc)
 
 
 def ring_attn_plan(P, dev0, n_local, n, *, causal=False, striped=False, layout=None) -> np.ndarray:

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -252,6 +253,30 @@ hipError_t poison(const HopStress& hs, void* p, size_t bytes, hipStream_t stream
 
 hipError_t jitter(bool on, hipStream_t stream) { return on ? ra::launch_spin(kJitterRounds, stream) : hipSuccess; }
 
+// Fixed device scratch of ring_attn_local_noalloc: the ring's receive slots and running state live
+// here instead of in a caller workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device memory: kernel
+// arguments and copies use the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxGpus = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxGpus] = {};
+
+// Device address of `scratch` on the current device (looked up once per device); null on failure.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxGpus) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,6 +289,7 @@ const char* ring_attn_strerror(int code) {
     case RA_ERR_HIP: return "HIP runtime error";
     case RA_ERR_WORKSPACE: return "workspace too small";
     case RA_ERR_INJECTED: return "stopped by RING_ATTN_FAIL_AT_STEP";
+    case RA_ERR_SCRATCH: return "needs more than the fixed scratch of ring_attn_local_noalloc";
     default: return "unknown status";
   }
 }
@@ -481,13 +507,15 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
     }                          \
   } while (0)
 
-  for (int a = 0; a < 2; ++a) {
-    RA_CHECK(hipEventCreateWithFlags(&ev_copy[a], hipEventDisableTiming));
-    RA_CHECK(hipEventCreateWithFlags(&ev_comp[a], hipEventDisableTiming));
-  }
-  RA_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
+  // cross-stream ordering needs events only when the copies have a stream of their own; on one
+  // stream, stream order alone separates every copy from the kernels around it
   const bool two_streams = xs != cs;
   if (two_streams) {
+    for (int a = 0; a < 2; ++a) {
+      RA_CHECK(hipEventCreateWithFlags(&ev_copy[a], hipEventDisableTiming));
+      RA_CHECK(hipEventCreateWithFlags(&ev_comp[a], hipEventDisableTiming));
+    }
+    RA_CHECK(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
     RA_CHECK(hipEventRecord(ev_fork, cs));
     RA_CHECK(hipStreamWaitEvent(xs, ev_fork, 0));
   }
@@ -572,19 +600,19 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   if (kv_src_is_host && stop > 0) {
     RA_CHECK(jitter(hs.jitter_copy, xs));
     RA_CHECK(enqueue_hop(0));
-    RA_CHECK(hipEventRecord(ev_copy[0], xs));
+    if (two_streams) RA_CHECK(hipEventRecord(ev_copy[0], xs));
   }
   for (int s = 0; s < stop; ++s) {
     // copies for step s+1, into the slot that step s-1 read; they may read blocks that kernel s-1
     // handed over, so they wait for it
     if (s + 1 < stop && needs_copy(s + 1)) {
-      if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
+      if (s >= 1 && two_streams) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
       RA_CHECK(jitter(hs.jitter_copy, xs));
       RA_CHECK(enqueue_hop(s + 1));
-      RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
+      if (two_streams) RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
     }
     const bool staged = kv_src_is_host || s > 0;
-    if (needs_copy(s)) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
+    if (needs_copy(s) && two_streams) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
 
     StepParams p{};
     p.q = q_local;
@@ -641,7 +669,7 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
       hipEvent_t e1 = step_events && ch + 1 == n_chunks ? (hipEvent_t)step_events[2 * s + 1] : nullptr;
       RA_CHECK(launch_step(p, dtype, cs, e0, e1));
     }
-    if (s + 2 < stop && needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+    if (s + 2 < stop && needs_copy(s + 2) && two_streams) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
   if (stop < P) {
     // stopped before step `stop`: the workspace state is the fold of steps [0, stop); devices that
@@ -681,6 +709,23 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
   cleanup();
 #undef RA_CHECK
   return RA_OK;
+}
+
+size_t ring_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int ring_attn_local_noalloc(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
+                            float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
+                            float scale, int mask, int layout, void* compute_stream, void* copy_stream,
+                            void* const* step_events) {
+  const size_t need = ring_attn_local_workspace_bytes(P, n_local, B, Hq, Hkv, n, D, dtype);
+  if (need == 0)  // invalid arguments, or nothing to do: ring_attn_local says which, before any HIP call
+    return ring_attn_local(q_local, k_src, v_src, kv_src_is_host, o, lse, P, dev0, n_local, B, Hq, Hkv, n, D, dtype,
+                           scale, mask, layout, nullptr, 0, compute_stream, copy_stream, step_events);
+  if (need > kNoAllocScratchBytes) return RA_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return RA_ERR_HIP;
+  return ring_attn_local(q_local, k_src, v_src, kv_src_is_host, o, lse, P, dev0, n_local, B, Hq, Hkv, n, D, dtype,
+                         scale, mask, layout, ws, kNoAllocScratchBytes, compute_stream, copy_stream, step_events);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -89,6 +89,7 @@ extern "C" {
 #define RA_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
 #define RA_ERR_WORKSPACE (-4)   /* workspace too small */
 #define RA_ERR_INJECTED (-5)    /* ring_attn_local stopped early by RING_ATTN_FAIL_AT_STEP (test hook) */
+#define RA_ERR_SCRATCH (-6)     /* larger than the fixed scratch of ring_attn_local_noalloc */
 
 /* ring_attn_step flags */
 #define RA_STEP_INIT 1 /* ignore the incoming state: treat it as m = -inf, l = 0, o_acc = 0 */
@@ -208,6 +209,30 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
  * "Como funciona a atenção em anel": the accumulated sums each device keeps).  Pure host
  * arithmetic; no HIP call. */
 size_t ring_attn_local_workspace_bytes(int P, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype);
+
+/*
+ * ring_attn_local_noalloc — ring_attn_local without a workspace argument and without any device
+ * memory allocation, for callers that cannot allocate: code recorded under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc.  Same arguments, schedule, kernels and results
+ * as ring_attn_local, except that the receive slots and the running state live in a fixed device
+ * array inside the library (ring_attn_noalloc_scratch_bytes() bytes, 64 MiB, one copy per GPU, held
+ * until the process ends); the caller still passes every input and output.
+ *   - Returns RA_ERR_SCRATCH when ring_attn_local_workspace_bytes(...) for these arguments exceeds
+ *     that size, RA_ERR_INVALID_ARG / RA_ERR_UNSUPPORTED as ring_attn_local, RA_ERR_HIP if the array's
+ *     device address cannot be obtained.
+ *   - The first call on a device looks up the array's address there (hipGetSymbolAddress); no call
+ *     allocates device memory.  With compute_stream == copy_stream no HIP event is created either.
+ *   - Every call on one GPU uses the same array and nothing in it needs clearing between calls (each
+ *     ring initialises the state it reads).  Calls that overlap on one GPU (concurrent streams, or
+ *     another thread) race on it: the caller serialises them.
+ */
+int ring_attn_local_noalloc(const void* q_local, const void* k_src, const void* v_src, int kv_src_is_host, void* o,
+                            float* lse, int P, int dev0, int n_local, int B, int Hq, int Hkv, int n, int D, int dtype,
+                            float scale, int mask, int layout, void* compute_stream, void* copy_stream,
+                            void* const* step_events);
+
+/* Size in bytes of the fixed scratch ring_attn_local_noalloc works in (host constant). */
+size_t ring_attn_noalloc_scratch_bytes(void);
 
 /*
  * ring_attn_plan — the ring schedule as a table, computed on the host (no HIP call): the N steps of

@@ -33,6 +33,8 @@ def test_strerror():
     assert "invalid" in ra.ring_attn_strerror(-1)
     assert "unsupported" in ra.ring_attn_strerror(-2)
     assert "workspace" in ra.ring_attn_strerror(-4)
+    assert "RING_ATTN_FAIL_AT_STEP" in ra.ring_attn_strerror(-5)
+    assert "scratch" in ra.ring_attn_strerror(-6)
     assert ra.ring_attn_strerror(12345) == "unknown status"
 
 
@@ -173,6 +175,28 @@ def test_local_rejects_bad_arguments_and_small_workspace():
     assert call(q=None) == -1
     assert call(n=0) == 0               # nothing to do
     assert ra.ring_attn_local_workspace_bytes(4, 5, 1, 2, 1, 8, 16, 0) == 0
+
+
+def test_noalloc_scratch_size_and_rejections():
+    """ring_attn_local_noalloc's fixed scratch is 64 MiB; a ring whose workspace would not fit is refused
+    with RA_ERR_SCRATCH and invalid shapes with RA_ERR_INVALID_ARG, both before any HIP call."""
+    L = ra.lib()
+    assert ra.ring_attn_noalloc_scratch_bytes() == 64 << 20
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE * 8, v=FAKE * 16, host=0, o=FAKE * 24, lse=None, P=4, dev0=0, n_local=4, B=1, Hq=2,
+                 Hkv=1, n=8, D=16, dtype=0, scale=0.25, mask=0, layout=0)
+        a.update(kw)
+        return L.ring_attn_local_noalloc(a["q"], a["k"], a["v"], a["host"], a["o"], a["lse"], a["P"], a["dev0"],
+                                         a["n_local"], a["B"], a["Hq"], a["Hkv"], a["n"], a["D"], a["dtype"],
+                                         a["scale"], a["mask"], a["layout"], None, None, None)
+
+    # 8 devices of 8192 tokens, 8 heads, D = 128, bf16: 512 MiB of slots alone
+    assert ra.ring_attn_local_workspace_bytes(8, 8, 1, 8, 8, 8192, 128, 1) > 64 << 20
+    assert call(P=8, n_local=8, Hq=8, Hkv=8, n=8192, D=128, dtype=1) == -6
+    assert call(P=0) == -1 and call(n_local=5) == -1 and call(Hq=3, Hkv=2) == -1
+    assert call(D=256) == -2            # as ring_attn_local
+    assert call(n=0) == 0               # nothing to do
 
 
 def test_plan_rejects_bad_arguments():
