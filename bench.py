@@ -2,9 +2,9 @@
 """Benchmark of the per-device ring-attention hot path on one MI355X.
 
 One benchmark step = one call of ``ring_attn_local``: the whole P-step ring (one batched step kernel
-per ring step that also hands each device's block to its successor, copies on a second stream for
-the blocks it cannot, the final division fused into each device's last step) over one batch of
-seeded synthetic input already resident in HBM.
+per two ring steps, which folds each device's block and its predecessor's and hands the latter on to
+the successor; copies on a second stream for the blocks it cannot hand on; the final division fused
+into each device's last step) over one batch of seeded synthetic input already resident in HBM.
 
 The default workload is the non-causal bf16 configuration the headline metric is quoted on
 (B=1, S=16384 as 8 shards of 2048, 8 heads, D=128, all 8 devices on the one GPU).  The causal
@@ -46,6 +46,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc"
                   for f in ("step_mfma_bf16.hip", "gfx950_tile.h", "internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
 EVENT_EVERY = 4  # timed calls between two that carry per-step kernel events
+LAUNCH_MIN_MS = 0.02  # an event interval shorter than this holds no step kernel
 
 
 def log(msg):
@@ -144,22 +145,28 @@ def run_workload(w, steps, warmup, measure_clock=True):
     ms = total_ms / steps
     per_call = sorted(bounds[i].elapsed_ms(bounds[i + 1]) for i in range(steps))
 
-    # algorithmic FLOPs per ring step launch (all local devices of that step)
-    per_launch = []
+    # algorithmic FLOPs per ring step (all local devices of that step)
+    per_step = []
     for s in range(w.P):
         pairs = 0
         for i in range(dev0, dev0 + n_local):
             pairs += ra.ring_attn_visible_pairs(w.P, n, i, (i - s) % w.P, causal=causal, layout=w.layout)
-        per_launch.append(4.0 * w.D * w.Hq * w.B * pairs)
-    flops = sum(per_launch)
+        per_step.append(4.0 * w.D * w.Hq * w.B * pairs)
+    flops = sum(per_step)
     assert abs(flops - w.flops()) <= 1e-6 * flops, (flops, w.flops())
     kernel_ms = [[ev[i][2 * s].elapsed_ms(ev[i][2 * s + 1]) for s in range(w.P)] for i in sampled]
-    launch_ms = [sum(k[s] for k in kernel_ms) / len(kernel_ms) for s in range(w.P)]
+    step_ms = [sum(k[s] for k in kernel_ms) / len(kernel_ms) for s in range(w.P)]
+    # a launch that folds steps s and s+1 stamps the events of step s; those of step s+1 are recorded
+    # right after it (an interval of a few microseconds, no kernel); steps with nothing to compute
+    # record theirs on the stream too.  Launches = the steps whose interval holds a kernel.
+    starts = [s for s in range(w.P) if step_ms[s] > LAUNCH_MIN_MS] or [0]
+    launch_ms = [step_ms[s] for s in starts]
+    launch_flops = [sum(per_step[s:(starts[a + 1] if a + 1 < len(starts) else w.P)]) for a, s in enumerate(starts)]
     kernel_total_ms = sum(launch_ms)
     achieved = flops / (kernel_total_ms * 1e-3) / 1e12  # flop-weighted average over the step launches
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak); "
-        f"step kernels {kernel_total_ms:.3f} ms ({achieved:.1f} TFLOP/s), per step "
+        f"step kernels {kernel_total_ms:.3f} ms in {len(starts)} launches ({achieved:.1f} TFLOP/s), per launch "
         + ", ".join(f"{x:.3f}" for x in launch_ms))
     sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
     if sclk:
@@ -167,7 +174,7 @@ def run_workload(w, steps, warmup, measure_clock=True):
     res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
                ms_min=per_call[0], tflops=tflops,
                flops=flops, kernel_ms=kernel_total_ms, kernel_tflops=achieved, launch_ms=launch_ms,
-               launch_flops=per_launch, sclk_mhz=sclk, sclk_busy=busy)
+               launch_flops=launch_flops, sclk_mhz=sclk, sclk_busy=busy)
     del tq, tk, tv, o, lse, ws
     torch.cuda.empty_cache()
     return res
@@ -388,6 +395,19 @@ def traffic_entry():
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model_name():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, seconds):
     """Time the float64 CPU oracle on a bounded sample of the workload's query rows."""
     import numpy as np
@@ -400,6 +420,7 @@ def cpu_baseline(w, seconds):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    cpu_model = cpu_model_name()
     if w.local_shard is not None or w.layout != "contiguous":
         raise ValueError("the CPU baseline samples token-order queries of a whole-sequence workload")
     q, k, v = si.workload_qkv(w)
@@ -427,7 +448,7 @@ def cpu_baseline(w, seconds):
             break
         nrows = int(min(total, nrows * max(2.0, min(8.0, seconds / max(dt, 1e-3)))))
     fl = 4.0 * w.D * visible(rows)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{nrows} random (head, token) rows of {w.name}, float64 NumPy, {dt:.1f} s"}
 
 
@@ -438,7 +459,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
-    ap.add_argument("--extra", default="causal_striped_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
+    ap.add_argument("--extra", default="causal_striped_64k,causal_contig_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
                     "bwd_noncausal_16k,bwd_causal_striped_64k,bwd_causal_zigzag_64k,ffn_16k,ffn_32h_4k",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -503,7 +524,9 @@ def main():
             "traffic": traffic,
             "frac_at_sclk": (main_res["kernel_tflops"] / clock_peak(main_res["sclk_mhz"])
                              if main_res["sclk_mhz"] else None),
-            "flops_per_launch": main_res["launch_flops"][0], "avg_launch_ms": sum(main_res["launch_ms"]) / w.P}
+            "flops_per_launch": sum(main_res["launch_flops"]) / len(main_res["launch_flops"]),
+            "launches": len(main_res["launch_ms"]),
+            "avg_launch_ms": sum(main_res["launch_ms"]) / len(main_res["launch_ms"])}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -514,7 +537,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "P": w.P, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "mask": "causal" if w.causal else "none", "layout": w.layout,
-                   "hops": "inside the step kernel (LDS rows stored into the successor's slot); copies otherwise"},
+                   "steps_per_launch": 2,
+                   "hops": "two ring steps per launch: the second block pulled from the predecessor's slot, "
+                           "pushed on from LDS into the successor's next slot; copies where the kernel cannot"},
         "pct_of_peak": 100 * main_res["tflops"] / PEAK_BF16_TFLOPS,
         "ms_per_step_median": main_res["ms_median"], "ms_per_step_min": main_res["ms_min"],
         "sclk_mhz": main_res["sclk_mhz"],

@@ -277,6 +277,225 @@ void* device_scratch() {
   return g_scratch_ptr[dev];
 }
 
+// Ring steps folded per launch of the bf16 D=128 kernel when the whole ring is local (1 or 2;
+// RING_ATTN_STEPS_PER_LAUNCH overrides the default of 2).
+int steps_per_launch() {
+  if (const char* e = std::getenv("RING_ATTN_STEPS_PER_LAUNCH")) {
+    if (e[0] == '1' && e[1] == 0) return 1;
+  }
+  return 2;
+}
+
+// Everything the whole-ring drivers share once the arguments are validated.
+struct LocalRing {
+  const void* q;
+  const char* ksrc;
+  const char* vsrc;
+  void* o;
+  float* lse;
+  int P, B, Hq, Hkv, n, D, dtype, layout;
+  bool causal;
+  float scale_log2;
+  size_t blk;
+  char* stage_k[2];
+  char* stage_v[2];
+  float* o_acc;
+  float* m;
+  float* l;
+  hipStream_t cs, xs;
+  void* const* step_events;
+  HopStress hs;
+};
+
+// The whole ring with two steps per launch (every device local, key/value source in device memory,
+// the bf16 D=128 kernel).  Launch L folds steps s = 2L and s + 1: device i first folds the block it
+// holds (receive slot L & 1 of device i, or its own shard at L = 0) and then the block its
+// predecessor holds at step s (slot L & 1 of device i - 1, or shard i - 1 at L = 0; one hop, pulled
+// by the reader), with the running state in registers across both; the second block is what device i
+// holds at step s + 1, and it also passes it on: stored from inside the kernel into the successor's
+// slot (L + 1) & 1 (one hop, pushed), or, where the kernel cannot (the block is not computed, the
+// forwarding workgroups do not stage all of it, or zigzag's half-block units), copied there on the
+// copy stream.  Slot L & 1 is only read and slot (L + 1) & 1 only written during launch L, so a
+// launch never waits on another workgroup; two hops per launch is the most a neighbour-only ring
+// allows without such waits.  Returns a hipError_t.
+hipError_t ring_two_step(const LocalRing& r, const std::vector<int>& cls, const std::vector<int>& first_step,
+                         const std::vector<int>& last_step, int nh) {
+  const int P = r.P, n = r.n;
+  const int n_units = P * nh;
+  const int NL = (P + 1) / 2;
+  const int64_t st = layout_stride(r.layout, P);
+  const hipStream_t cs = r.cs, xs = r.xs;
+  const bool two_streams = xs != cs;
+  auto blockj = [&](int i, int s) { return ((i - s) % P + P) % P; };
+
+  // in-kernel push of launch L by device i (its step-(2L+1) block into device i+1's slot (L+1) & 1)
+  std::vector<uint8_t> push((size_t)NL * P, 0);
+  for (int L = 0; L + 1 < NL; ++L)
+    for (int i = 0; i < P && nh == 1; ++i) {
+      const int s1 = 2 * L + 1;
+      if (cls[(size_t)s1 * n_units + i] == 0) continue;
+      const int j = blockj(i, s1);
+      if (step_forward_covers(r.causal, block_offset(r.layout, P, n, i), st, n, block_offset(r.layout, P, n, j), st, n))
+        push[(size_t)L * P + i] = 1;
+    }
+  auto needs_copy = [&](int L) -> bool {  // launch L's slot L & 1 has a block not pushed by launch L-1
+    if (L <= 0 || L >= NL) return false;
+    for (int x = 0; x < P; ++x)
+      if (!push[(size_t)(L - 1) * P + (x + P - 1) % P]) return true;
+    return false;
+  };
+  // copies that fill slot L & 1 for launch L >= 1: device x's block of step 2L is the step-(2L-1)
+  // block of device x-1, which it read from slot (L-1) & 1 of device x-2 (or shard x-2 when L = 1)
+  auto enqueue_copies = [&](int L) -> hipError_t {
+    hipError_t e;
+    for (int x = 0; x < P; ++x) {
+      if (push[(size_t)(L - 1) * P + (x + P - 1) % P]) continue;
+      const int from = (x + P - 2) % P;
+      const char* ks = (L == 1 ? r.ksrc : r.stage_k[(L - 1) & 1]) + (size_t)from * r.blk;
+      const char* vs = (L == 1 ? r.vsrc : r.stage_v[(L - 1) & 1]) + (size_t)from * r.blk;
+      char* kd = r.stage_k[L & 1] + (size_t)x * r.blk;
+      char* vd = r.stage_v[L & 1] + (size_t)x * r.blk;
+      if ((e = poison(r.hs, kd, r.blk, xs)) != hipSuccess) return e;
+      if ((e = poison(r.hs, vd, r.blk, xs)) != hipSuccess) return e;
+      if ((e = hipMemcpyAsync(kd, ks, r.blk, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
+      if ((e = hipMemcpyAsync(vd, vs, r.blk, hipMemcpyDeviceToDevice, xs)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+
+  hipEvent_t ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr}, ev_fork = nullptr;
+  hipError_t err = hipSuccess;
+  auto cleanup = [&]() {
+    for (int a = 0; a < 2; ++a) {
+      if (ev_copy[a]) (void)hipEventDestroy(ev_copy[a]);
+      if (ev_comp[a]) (void)hipEventDestroy(ev_comp[a]);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+  };
+#define RA_TRY(x)               \
+  do {                          \
+    if ((err = (x)) != hipSuccess) { \
+      cleanup();                \
+      return err;               \
+    }                           \
+  } while (0)
+  if (two_streams) {
+    for (int a = 0; a < 2; ++a) {
+      RA_TRY(hipEventCreateWithFlags(&ev_copy[a], hipEventDisableTiming));
+      RA_TRY(hipEventCreateWithFlags(&ev_comp[a], hipEventDisableTiming));
+    }
+    RA_TRY(hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming));
+    RA_TRY(hipEventRecord(ev_fork, cs));
+    RA_TRY(hipStreamWaitEvent(xs, ev_fork, 0));
+  }
+  for (int L = 0; L < NL; ++L) {
+    const int s0 = 2 * L, s1 = 2 * L + 1;
+    // copies for launch L+1 into the slot launch L-1 read (they may read blocks it pushed)
+    if (needs_copy(L + 1)) {
+      if (L >= 1 && two_streams) RA_TRY(hipStreamWaitEvent(xs, ev_comp[(L + 1) & 1], 0));
+      RA_TRY(jitter(r.hs.jitter_copy, xs));
+      RA_TRY(enqueue_copies(L + 1));
+      if (two_streams) RA_TRY(hipEventRecord(ev_copy[(L + 1) & 1], xs));
+    }
+    if (needs_copy(L) && two_streams) RA_TRY(hipStreamWaitEvent(cs, ev_copy[L & 1], 0));
+
+    StepParams p{};
+    p.q = r.q;
+    // source 0: the shards in place; 1: the slot of this launch; 2: the slot of the next
+    p.kv_base[0][0] = (char*)r.ksrc;
+    p.kv_base[0][1] = (char*)r.vsrc;
+    p.kv_base[1][0] = r.stage_k[L & 1];
+    p.kv_base[1][1] = r.stage_v[L & 1];
+    p.kv_base[2][0] = r.stage_k[(L + 1) & 1];
+    p.kv_base[2][1] = r.stage_v[(L + 1) & 1];
+    p.kv_block = (int64_t)r.blk;
+    p.o_acc = r.o_acc;
+    p.m = r.m;
+    p.l = r.l;
+    p.o_out = r.o;
+    p.lse_out = r.lse;
+    p.B = r.B;
+    p.Hq = r.Hq;
+    p.Hkv = r.Hkv;
+    p.Nq = n / nh;
+    p.NqTot = n;
+    p.NkTot = n;
+    p.D = r.D;
+    p.causal = r.causal ? 1 : 0;
+    p.scale_log2 = r.scale_log2;
+    std::vector<int> todo;
+    for (int u = 0; u < n_units; ++u) {
+      const bool c0 = cls[(size_t)s0 * n_units + u] != 0;
+      const bool c1 = s1 < P && cls[(size_t)s1 * n_units + u] != 0;
+      if (c0 || c1) todo.push_back(u);
+    }
+    const size_t n_chunks = todo.empty() ? 1 : (todo.size() + RA_MAX_DEV - 1) / RA_MAX_DEV;
+    for (size_t ch = 0; ch < n_chunks; ++ch) {
+      p.n_launch = 0;
+      p.Nk = 0;
+      for (size_t a = ch * RA_MAX_DEV; a < todo.size() && a < (ch + 1) * RA_MAX_DEV; ++a) {
+        const int u = todo[a], i = u / nh;
+        const int x = p.n_launch++;
+        p.slot[x] = i;
+        p.nsub[x] = 0;
+        for (int s = s0; s <= s1 && s < P; ++s) {
+          if (cls[(size_t)s * n_units + u] == 0) continue;
+          const int j = blockj(i, s);
+          const Unit un = ring_unit(r.causal, r.layout, P, n, i, j, u % nh);
+          const int b = p.nsub[x]++;
+          // step s0: the block device i holds; step s1: the block device i - 1 holds at step s0
+          const int holder = s == s0 ? i : (i + P - 1) % P;
+          p.kv[x][b] = L == 0 ? ra::kv_ref(0, holder) : ra::kv_ref(1, holder);
+          p.nk[x][b] = un.nk;
+          p.k_off[x][b] = un.k_off;
+          p.Nk = std::max(p.Nk, un.nk);
+          p.q_row0[x] = un.row0;
+          p.q_off[x] = un.q_off;
+          p.q_stride = un.stride;  // the same for every unit of a layout
+          p.k_stride = un.stride;
+        }
+        const bool first = first_step[u] == s0 || first_step[u] == s1;
+        const bool last = last_step[u] == s0 || last_step[u] == s1;
+        p.dflags[x] = (first ? ra::kDevInit : 0) | (last ? ra::kDevFinal : 0);
+        const bool pushes = push[(size_t)L * P + i] != 0;
+        p.fwd[x] = pushes ? ra::kv_ref(2, (i + 1) % P) : -1;
+        if (pushes) {  // slot (L+1) & 1 was last read by launch L-1, earlier on this stream
+          RA_TRY(poison(r.hs, r.stage_k[(L + 1) & 1] + (size_t)((i + 1) % P) * r.blk, r.blk, cs));
+          RA_TRY(poison(r.hs, r.stage_v[(L + 1) & 1] + (size_t)((i + 1) % P) * r.blk, r.blk, cs));
+        }
+      }
+      RA_TRY(jitter(r.hs.jitter_compute, cs));
+      hipEvent_t e0 = r.step_events && ch == 0 ? (hipEvent_t)r.step_events[2 * s0] : nullptr;
+      hipEvent_t e1 = r.step_events && ch + 1 == n_chunks ? (hipEvent_t)r.step_events[2 * s0 + 1] : nullptr;
+      RA_TRY(launch_step(p, r.dtype, cs, e0, e1));
+    }
+    if (r.step_events && s1 < P) {  // the second step's events: right after the launch that folded it
+      RA_TRY(hipEventRecord((hipEvent_t)r.step_events[2 * s1], cs));
+      RA_TRY(hipEventRecord((hipEvent_t)r.step_events[2 * s1 + 1], cs));
+    }
+    if (needs_copy(L + 2) && two_streams) RA_TRY(hipEventRecord(ev_comp[L & 1], cs));
+  }
+  // devices that never computed (no visible block): empty output
+  for (int t = 0; t < P && nh == 1; ++t)
+    if (first_step[t] < 0) {
+      int slot_t = t;
+      RA_TRY(ra::launch_init_state(r.o_acc, r.m, r.l, P, &slot_t, 1, r.B, r.Hq, n, r.D, cs));
+      const size_t per = (size_t)r.B * r.Hq * n;
+      RA_TRY(ra::launch_finalize(r.o_acc + t * per * r.D, r.m + t * per, r.l + t * per,
+                                 (char*)r.o + t * per * r.D * elem_size(r.dtype), r.lse ? r.lse + t * per : nullptr, 1,
+                                 r.B, r.Hq, n, r.D, r.dtype, cs));
+    }
+  if (two_streams) {
+    RA_TRY(hipEventRecord(ev_copy[0], xs));
+    RA_TRY(hipStreamWaitEvent(cs, ev_copy[0], 0));
+    RA_TRY(hipEventRecord(ev_comp[0], cs));
+    RA_TRY(hipStreamWaitEvent(xs, ev_comp[0], 0));
+  }
+  cleanup();
+#undef RA_TRY
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,8 +573,9 @@ int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, fl
 
   StepParams p{};
   p.q = q;
-  p.k = k;
-  p.v = v;
+  p.kv_base[0][0] = (char*)k;  // read only: no slot of this launch forwards
+  p.kv_base[0][1] = (char*)v;
+  p.kv_block = (int64_t)B * Nk * Hkv * D * es;
   p.o_acc = o_acc;
   p.m = m;
   p.l = l;
@@ -382,9 +602,12 @@ int ring_attn_step(const void* q, const void* k, const void* v, float* o_acc, fl
     const int i = p.n_launch++;
     p.slot[i] = t;
     p.q_row0[i] = 0;
-    p.nk[i] = Nk;
     p.q_off[i] = qo;
-    p.k_off[i] = ko;
+    p.nsub[i] = 1;
+    p.kv[i][0] = ra::kv_ref(0, t);
+    p.nk[i][0] = Nk;
+    p.k_off[i][0] = ko;
+    p.fwd[i] = -1;
     p.dflags[i] = (flags & RA_STEP_INIT) ? ra::kDevInit : 0;
   }
   hipStream_t st = (hipStream_t)stream;
@@ -489,6 +712,30 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
         last_step[u] = s;
       }
     }
+
+  // whole ring local, device source, MFMA kernel: two ring steps per launch
+  if (!kv_src_is_host && uses_mfma_kernel(dtype, D) && n_local == P && P >= 2 && stop == P &&
+      steps_per_launch() == 2) {
+    LocalRing r{};
+    r.q = q_local;
+    r.ksrc = (const char*)k_src;
+    r.vsrc = (const char*)v_src;
+    r.o = o;
+    r.lse = lse;
+    r.P = P, r.B = B, r.Hq = Hq, r.Hkv = Hkv, r.n = n, r.D = D, r.dtype = dtype, r.layout = layout;
+    r.causal = causal;
+    r.scale_log2 = (float)(scale * kLog2e);
+    r.blk = blk;
+    for (int a = 0; a < 2; ++a) {
+      r.stage_k[a] = stage_k[a];
+      r.stage_v[a] = stage_v[a];
+    }
+    r.o_acc = o_acc, r.m = m_st, r.l = l_st;
+    r.cs = cs, r.xs = xs;
+    r.step_events = step_events;
+    r.hs = hs;
+    return hip_status(ring_two_step(r, cls, first_step, last_step, nh));
+  }
 
   hipEvent_t ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr}, ev_fork = nullptr;
   auto cleanup = [&]() {
@@ -616,8 +863,13 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
 
     StepParams p{};
     p.q = q_local;
-    p.k = staged ? (const void*)stage_k[s & 1] : (const void*)(ksrc + (size_t)dev0 * blk);
-    p.v = staged ? (const void*)stage_v[s & 1] : (const void*)(vsrc + (size_t)dev0 * blk);
+    // source 0: the blocks of step s (receive slot s & 1, or the shards in place); source 1: the other
+    // receive slot, which the in-step hop fills for step s + 1
+    p.kv_base[0][0] = staged ? stage_k[s & 1] : (char*)(ksrc + (size_t)dev0 * blk);
+    p.kv_base[0][1] = staged ? stage_v[s & 1] : (char*)(vsrc + (size_t)dev0 * blk);
+    p.kv_base[1][0] = stage_k[(s + 1) & 1];
+    p.kv_base[1][1] = stage_v[(s + 1) & 1];
+    p.kv_block = (int64_t)blk;
     p.o_acc = o_acc;
     p.m = m_st;
     p.l = l_st;
@@ -648,20 +900,21 @@ int ring_attn_local(const void* q_local, const void* k_src, const void* v_src, i
         const int x = p.n_launch++;
         p.slot[x] = t;
         p.q_row0[x] = un.row0;
-        p.nk[x] = un.nk;
-        p.Nk = std::max(p.Nk, un.nk);
         p.q_off[x] = un.q_off;
-        p.k_off[x] = un.k_off;
+        p.nsub[x] = 1;
+        p.kv[x][0] = ra::kv_ref(0, t);
+        p.nk[x][0] = un.nk;
+        p.k_off[x][0] = un.k_off;
+        p.Nk = std::max(p.Nk, un.nk);
         p.q_stride = un.stride;  // the same for every unit of a layout
         p.k_stride = un.stride;
         p.dflags[x] = (s == first_step[u] ? ra::kDevInit : 0) |
                       (s == last_step[u] && stop == P ? ra::kDevFinal : 0);
         const int succ = in_step_hop ? fwd_to[(size_t)s * n_local + t] : -1;
-        p.fwd_k[x] = succ >= 0 ? (void*)(stage_k[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
-        p.fwd_v[x] = succ >= 0 ? (void*)(stage_v[(s + 1) & 1] + (size_t)succ * blk) : nullptr;
+        p.fwd[x] = succ >= 0 ? ra::kv_ref(1, succ) : -1;
         if (succ >= 0) {  // the slot this kernel fills was last read by step s-1, earlier on this stream
-          RA_CHECK(poison(hs, p.fwd_k[x], blk, cs));
-          RA_CHECK(poison(hs, p.fwd_v[x], blk, cs));
+          RA_CHECK(poison(hs, stage_k[(s + 1) & 1] + (size_t)succ * blk, blk, cs));
+          RA_CHECK(poison(hs, stage_v[(s + 1) & 1] + (size_t)succ * blk, blk, cs));
         }
       }
       RA_CHECK(jitter(hs.jitter_compute, cs));

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   if (qr >= p.Nq) return;  // whole 16-lane groups leave together
   const int D = p.D, Hq = p.Hq, Hkv = p.Hkv;
   const int dev = p.slot[dl];
-  const int Nk = p.nk[dl], NqT = p.NqTot, NkT = p.NkTot, row = p.q_row0[dl] + qr;  // array row of this query
+  const int Nk = p.nk[dl][0], NqT = p.NqTot, NkT = p.NkTot, row = p.q_row0[dl] + qr;  // array row of this query
   const int dfl = p.dflags[dl];
   const int kvh = h / (Hq / Hkv);
 
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
 
   int kmax = Nk - 1;
   if (p.causal) {
-    const int64_t dpos = p.q_off[dl] + (int64_t)qr * p.q_stride - p.k_off[dl];
+    const int64_t dpos = p.q_off[dl] + (int64_t)qr * p.q_stride - p.k_off[dl][0];
     if (dpos < 0) {
       kmax = -1;
     } else {
@@ -79,13 +79,16 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
   const float c = p.scale_log2;
   float M = -INFINITY, l = 0.f;
   const size_t kvrow = (size_t)Hkv * D;
-  const size_t kvbase = ((size_t)dev * p.B + bb) * NkT * kvrow + (size_t)kvh * D;
+  const size_t kvbase = (size_t)bb * NkT * kvrow + (size_t)kvh * D;  // elements into this slot's block
+  const int ref = p.kv[dl][0];
+  const char* kblock = p.kv_base[ref >> 16][0] + (int64_t)(ref & 0xffff) * p.kv_block;
+  const char* vblock = p.kv_base[ref >> 16][1] + (int64_t)(ref & 0xffff) * p.kv_block;
   for (int u = 0; u <= kmax; ++u) {
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < kMaxPerLane; ++e) {
       const int d = sub + kLanesPerRow * e;
-      if (d < D) part = __builtin_fmaf(q[e], load_elem<BF16>(p.k, kvbase + u * kvrow + d), part);
+      if (d < D) part = __builtin_fmaf(q[e], load_elem<BF16>(kblock, kvbase + u * kvrow + d), part);
     }
 #pragma unroll
     for (int w = kLanesPerRow / 2; w >= 1; w /= 2) part += __shfl_xor(part, w, kLanesPerRow);
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void step_generic(const StepParams p) {
 #pragma unroll
     for (int e = 0; e < kMaxPerLane; ++e) {
       const int d = sub + kLanesPerRow * e;
-      if (d < D) o[e] = __builtin_fmaf(pr, load_elem<BF16>(p.v, kvbase + u * kvrow + d), o[e]);
+      if (d < D) o[e] = __builtin_fmaf(pr, load_elem<BF16>(vblock, kvbase + u * kvrow + d), o[e]);
     }
   }
 

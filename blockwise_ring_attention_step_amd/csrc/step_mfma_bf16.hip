@@ -1,7 +1,8 @@
 // bf16 ring-attention step kernel for gfx950 (CDNA4), head dim 128, on v_mfma_f32_32x32x16_bf16.
 //
-// One workgroup (8 waves, 512 threads) folds one key/value block into the online-softmax state of
-// 256 query rows of one (device, batch, query head).  This is the per-step work of the Ultralytics
+// One workgroup (8 waves, 512 threads) folds one or two key/value blocks (one or two ring steps) into
+// the online-softmax state of 256 query rows of one (device, batch, query head): the blocks form one
+// stream of 64-key tiles, and the state stays in registers across the seam.  This is the per-step work of the Ultralytics
 // glossary page "Ring Attention", section "Como funciona a atenção em anel" (attend the held block,
 // accumulate exponentiated scores and weighted values), with the running-maximum rescaling of
 // "Sequence Parallelism and Ring Attention", section "Approfondimento tecnico".
@@ -66,22 +67,46 @@ __device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
 // all but this wave's most recent tile request (2 K + 2 V instructions) have landed in LDS
 __device__ __forceinline__ void wait_vmem_but_one_tile() { wait_vmem<4>(); }
 
-// Largest key index visible to the query at local row `row` (causal), clamped to [-1, nk-1].
-__device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int row, int nk) {
+// Largest key index of block b visible to the query at local row `row` (causal), clamped to [-1, nk-1].
+__device__ __forceinline__ int last_visible_key(const StepParams& p, int dl, int b, int row, int nk) {
   const int64_t pq = p.q_off[dl] + (int64_t)row * p.q_stride;
-  const int64_t d = pq - p.k_off[dl];
+  const int64_t d = pq - p.k_off[dl][b];
   if (d < 0) return -1;
   const int64_t kk = d / p.k_stride;
   return kk < (int64_t)(nk - 1) ? (int)kk : nk - 1;
 }
 
-struct Ctx {
-  const char* kbase;   // this (device, batch, kv head)'s key rows, byte address of key 0
+// One key/value block the workgroup folds, and the loop bounds it sets.
+struct Block {
+  const char* kbase;  // this (batch, kv head)'s key rows in the block, byte address of key 0
   const char* vbase;
-  int64_t row_bytes;   // bytes between consecutive keys (Hkv * D * 2)
-  int nk;
-  uint32_t goff[kPiecesPerWave];  // byte offset of this lane's 16 B in each of its tile pieces
+  int nk;             // keys in the block
+  int ntiles;         // tiles the workgroup loads
+  int ntiles_grp;     // tiles this wave's group computes (causal: group A may stop earlier)
+  int nfull;          // tiles [0, nfull) need no mask for any row of the group
+  int kmax_lane;      // largest key this lane's query sees
 };
+
+// The workgroup's tile stream: virtual tile v < t0 is tile v of block 0, v in [t0, total) tile v - t0
+// of block 1 (a slot that folds two ring steps); the online-softmax state runs on across the seam.
+struct Ctx {
+  int64_t row_bytes;   // bytes between consecutive keys (Hkv * D * 2)
+  uint32_t goff[kPiecesPerWave];  // byte offset of this lane's 16 B in each of its tile pieces
+  Block b0, b1;  // b1 repeats b0 when the slot folds one block
+  int t0, total;
+};
+
+// Block and local tile index of virtual tile v (selects, no indexing).
+struct TileRef {
+  const char* kbase;
+  const char* vbase;
+  int nk, t;
+};
+__device__ __forceinline__ TileRef tile_ref(const Ctx& cx, int v) {
+  const bool second = v >= cx.t0;
+  return TileRef{second ? cx.b1.kbase : cx.b0.kbase, second ? cx.b1.vbase : cx.b0.vbase,
+                 second ? cx.b1.nk : cx.b0.nk, second ? v - cx.t0 : v};
+}
 
 
 // This wave's share of one K/V tile request: 2 K + 2 V copies of 1 KiB (the wait counts rely on
@@ -94,14 +119,15 @@ struct TileRequest {
   uint32_t off[kPiecesPerWave]; // per-lane byte offsets of the pieces
 };
 
-__device__ __forceinline__ TileRequest make_request(const Ctx& cx, int t, LDS_AS char* smem, int stage, int wave) {
+__device__ __forceinline__ TileRequest make_request(const Ctx& cx, int v, LDS_AS char* smem, int stage, int wave) {
   TileRequest r;
-  const int key0 = t * kBc;
+  const TileRef tr = tile_ref(cx, v);
+  const int key0 = tr.t * kBc;
   const int64_t tofs = (int64_t)key0 * cx.row_bytes;
-  r.kt = cx.kbase + tofs;
-  r.vt = cx.vbase + tofs;
+  r.kt = tr.kbase + tofs;
+  r.vt = tr.vbase + tofs;
   r.dst = (uint32_t)(uintptr_t)(smem + stage * kTileBytes) + wave * kPiecesPerWave * 1024;
-  if (key0 + kBc <= cx.nk) {
+  if (key0 + kBc <= tr.nk) {
 #pragma unroll
     for (int i = 0; i < kPiecesPerWave; ++i) r.off[i] = cx.goff[i];
   } else {  // ragged last tile: rows past the end re-read the last key (the mask drops them)
@@ -109,7 +135,7 @@ __device__ __forceinline__ TileRequest make_request(const Ctx& cx, int t, LDS_AS
 #pragma unroll
     for (int i = 0; i < kPiecesPerWave; ++i) {
       const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
-      const int krow = max(0, min(row, cx.nk - 1 - key0));
+      const int krow = max(0, min(row, tr.nk - 1 - key0));
       r.off[i] = (uint32_t)(krow * cx.row_bytes) + ((lane & 15) ^ swz(row)) * 16;
     }
   }
@@ -204,10 +230,6 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], int t, bool masked,
 }
 
 struct Loop {
-  int ntiles;      // tiles this workgroup loads
-  int ntiles_grp;  // tiles this wave's group computes (causal: group A may stop earlier)
-  int nfull;       // tiles [0, nfull) need no mask for any row of the group
-  int kmax_lane;
   int h2;
   float c;
 };
@@ -288,12 +310,18 @@ __device__ __forceinline__ void x_stream(const Frags& f, const LDS_AS char* smem
   x_stream_step<ST, 0>(f, smem, ring, s, pf, o, hook);
 }
 
-// Y_t: softmax of tile t.  A tile past this group's last visible key (causal, the group of lower
-// rows) is not needed: its P is zero, so the next window's P.V adds nothing.
-__device__ __forceinline__ void phase_y(const Loop& lp, int t, f32x16 (&s)[2], Softmax& sm, f32x16 (&o)[4],
-                                        bf16x8 (&pf)[4]) {
-  if (t < lp.ntiles_grp) {
-    tile_softmax(s, t, t >= lp.nfull, lp.kmax_lane, lp.h2, lp.c, sm, o, pf);
+// Y_v: softmax of virtual tile v.  A tile past this group's last visible key of its block (causal,
+// the group of lower rows) is not needed: its P is zero, so the next window's P.V adds nothing; nor
+// is the drain position v = total.
+__device__ __forceinline__ void phase_y(const Ctx& cx, const Loop& lp, int v, f32x16 (&s)[2], Softmax& sm,
+                                        f32x16 (&o)[4], bf16x8 (&pf)[4]) {
+  const bool second = v >= cx.t0;
+  const int t = second ? v - cx.t0 : v;
+  const int ntiles_grp = second ? cx.b1.ntiles_grp : cx.b0.ntiles_grp;
+  const int nfull = second ? cx.b1.nfull : cx.b0.nfull;
+  const int kmax_lane = second ? cx.b1.kmax_lane : cx.b0.kmax_lane;
+  if (v < cx.total && t < ntiles_grp) {
+    tile_softmax(s, t, t >= nfull, kmax_lane, lp.h2, lp.c, sm, o, pf);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pf[i] = bf16x8{};
@@ -316,21 +344,22 @@ __device__ __forceinline__ void window_end_x(bool drain) {
 // X_t), so no memory wait; forwarded rows may still be in flight and are covered by the next X end.
 __device__ __forceinline__ void window_end_y() { __syncthreads(); }
 
-// The ring hop inside the step: rows of the key/value block this workgroup forwards to the next
-// device's receive slot (its query tile's 256 keys, tiles [t_lo, t_hi)).
+// The ring hop inside the step: rows of the slot's last key/value block that this workgroup forwards to
+// the next device's receive slot (its query tile's 256 keys: virtual tiles [v_lo, v_hi) of the
+// stream, tile v - v0 of the block).
 struct Fwd {
   char* kdst;  // destination rows of this (batch, key/value head): key 0, K and V
   char* vdst;
-  int t_lo, t_hi;
+  int v_lo, v_hi, v0, nk;
 };
 
-// Forward tile t (stage ST): each lane stores back exactly the 16 bytes it copied into LDS, to the
-// same offset in the destination block; rows past the end of a ragged tile are not stored.
+// Forward virtual tile v (stage ST): each lane stores back exactly the 16 bytes it copied into LDS, to
+// the same offset in the destination block; rows past the end of a ragged tile are not stored.
 template <int ST>
-__device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const LDS_AS char* smem, int t,
+__device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const LDS_AS char* smem, int v,
                                              int wave) {
   const int lane = __lane_id();
-  const int key0 = t * kBc;
+  const int key0 = (v - fw.v0) * kBc;
   const int64_t tofs = (int64_t)key0 * cx.row_bytes;
 #pragma unroll
   for (int i = 0; i < kPiecesPerWave; ++i) {
@@ -338,7 +367,7 @@ __device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const
     const LDS_AS char* src = smem + ST * kTileBytes + (wave * kPiecesPerWave + i) * 1024 + 16 * lane;
     const i16x8 kd = *(const LDS_AS i16x8*)src;
     const i16x8 vd = *(const LDS_AS i16x8*)(src + kVRing);
-    if (key0 + row < cx.nk) {
+    if (key0 + row < fw.nk) {
       const int64_t off = tofs + (int64_t)row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16;
       *(i16x8*)(fw.kdst + off) = kd;
       *(i16x8*)(fw.vdst + off) = vd;
@@ -346,9 +375,9 @@ __device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const
   }
 }
 
-// Both barrier windows of position t (0 <= t <= ntiles, tile t in stage ST): request tile t+2,
+// Both barrier windows of position t (0 <= t <= total, virtual tile t in stage ST): request tile t+2,
 // then X_t = scores of tile t and P.V of tile t-1, then Y_t.  Every position runs the same X: at
-// position 0 the P.V multiplies a zeroed V stage by P = 0, and at position ntiles the scores are
+// position 0 the P.V multiplies a zeroed V stage by P = 0, and at position total the scores are
 // computed but never used, so the loop holds one X variant only.  Every wave runs this same
 // sequence; group B runs it one window behind group A (one extra barrier before the loop, and
 // group A one extra barrier after it), so in each window one group is in X while the other is in Y.
@@ -357,20 +386,20 @@ __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, cons
                                              int t, int wave, bf16x8 (&ring)[kRing], TileRequest& req,
                                              const Fwd& fw, f32x16 (&s)[2], bf16x8 (&pf)[4], Softmax& sm,
                                              f32x16 (&o)[4]) {
-  const bool drain = t + kPrefetch >= lp.ntiles;
+  const bool drain = t + kPrefetch >= cx.total;
   x_stream<ST>(f, smem, ring, s, pf, o, [&] {
     if (!drain)
 #pragma unroll
       for (int j = 0; j < 4; ++j) request_piece(req, j);
   });
   window_end_x(drain);
-  phase_y(lp, t, s, sm, o, pf);
+  phase_y(cx, lp, t, s, sm, o, pf);
   // the next X phase opens with the P.V of tile t, whose V rows both groups completed a window ago;
   // its tile request (tile t+3) is prepared here too, where the wave would wait at the barrier, and
   // so is the hop of tile t (this wave's copies of it completed at the end of X_{t-1})
   x_preload<(ST + 1) % kStages>(f, smem, ring);
   req = make_request(cx, t + 1 + kPrefetch, smem, (ST + 1 + kPrefetch) % kStages, wave);
-  if (t >= fw.t_lo && t < fw.t_hi) forward_tile<ST>(cx, fw, smem, t, wave);
+  if (t >= fw.v_lo && t < fw.v_hi) forward_tile<ST>(cx, fw, smem, t, wave);
   window_end_y();
 }
 
@@ -404,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   const int h = kvh * gsz + hq;
   const int dev = p.slot[dl];
   const int dfl = p.dflags[dl];
-  const int Nq = p.Nq, Nk = p.nk[dl], Hq = p.Hq;
+  const int Nq = p.Nq, Hq = p.Hq, nsub = p.nsub[dl];
   const int NqT = p.NqTot, NkT = p.NkTot, row0 = p.q_row0[dl];  // array rows; this slot's first row
 
   const int qrow0 = qt * kBr;
@@ -414,20 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   const int grow0 = min(qrow0 + (grp_b ? kBr / 2 : 0), qlast);  // this group's first and last rows
   const int grow1 = min(qrow0 + (grp_b ? kBr : kBr / 2) - 1, qlast);
 
-  // key ranges: the workgroup loads tiles up to its last row's limit; each group computes up to
-  // its own last row's limit; masks apply from the first tile its first row does not fully see
   Loop lp;
-  lp.kmax_lane = Nk - 1;
-  int kmin_grp = Nk - 1, kend_wg = Nk - 1, kend_grp = Nk - 1;
-  if (p.causal) {
-    lp.kmax_lane = last_visible_key(p, dl, qvalid ? qr : qlast, Nk);
-    kmin_grp = last_visible_key(p, dl, grow0, Nk);
-    kend_grp = last_visible_key(p, dl, grow1, Nk);
-    kend_wg = last_visible_key(p, dl, qlast, Nk);
-  }
-  lp.ntiles = kend_wg < 0 ? 0 : kend_wg / kBc + 1;
-  lp.ntiles_grp = kend_grp < 0 ? 0 : kend_grp / kBc + 1;
-  lp.nfull = kmin_grp < 0 ? 0 : (kmin_grp + 1) / kBc;
   lp.h2 = h2;
   lp.c = p.scale_log2;
 
@@ -442,28 +458,57 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     f.q[kk] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // ---- per-lane address tables
+  // ---- the blocks this slot folds: rows of this (batch, kv head), and the key ranges: the workgroup
+  // loads tiles up to its last row's limit; each group computes up to its own last row's limit; masks
+  // apply from the first tile its first row does not fully see
   Ctx cx;
-  const size_t kv_dev = (size_t)p.B * NkT * p.Hkv * kD;
-  const size_t kv_off = 2 * (dev * kv_dev + (size_t)bb * NkT * p.Hkv * kD + (size_t)kvh * kD);
-  cx.kbase = (const char*)p.k + kv_off;
-  cx.vbase = (const char*)p.v + kv_off;
+  const size_t kv_in_blk = 2 * ((size_t)bb * NkT * p.Hkv * kD + (size_t)kvh * kD);
   cx.row_bytes = (int64_t)p.Hkv * kD * 2;
-  cx.nk = Nk;
+  auto setup_block = [&](Block& bk, int bs) {
+    const int ref = p.kv[dl][bs];
+    const int64_t boff = (int64_t)(ref & 0xffff) * p.kv_block + (int64_t)kv_in_blk;
+    bk.kbase = p.kv_base[ref >> 16][0] + boff;
+    bk.vbase = p.kv_base[ref >> 16][1] + boff;
+    const int nk = p.nk[dl][bs];
+    bk.nk = nk;
+    bk.kmax_lane = nk - 1;
+    int kmin_grp = nk - 1, kend_wg = nk - 1, kend_grp = nk - 1;
+    if (p.causal) {
+      bk.kmax_lane = last_visible_key(p, dl, bs, qvalid ? qr : qlast, nk);
+      kmin_grp = last_visible_key(p, dl, bs, grow0, nk);
+      kend_grp = last_visible_key(p, dl, bs, grow1, nk);
+      kend_wg = last_visible_key(p, dl, bs, qlast, nk);
+    }
+    bk.ntiles = kend_wg < 0 ? 0 : kend_wg / kBc + 1;
+    bk.ntiles_grp = kend_grp < 0 ? 0 : kend_grp / kBc + 1;
+    bk.nfull = kmin_grp < 0 ? 0 : (kmin_grp + 1) / kBc;
+  };
+  setup_block(cx.b0, 0);
+  if (nsub > 1)
+    setup_block(cx.b1, 1);
+  else
+    cx.b1 = cx.b0;  // never reached: the stream ends at t0
+  cx.t0 = cx.b0.ntiles;
+  cx.total = cx.t0 + (nsub > 1 ? cx.b1.ntiles : 0);
 #pragma unroll
   for (int i = 0; i < kPiecesPerWave; ++i) {
     const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
     cx.goff[i] = (uint32_t)(row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16);
   }
+  // the hop inside the step: the slot's last block, this query tile's 256 keys of it
   Fwd fw;
   fw.kdst = fw.vdst = nullptr;
-  fw.t_lo = fw.t_hi = 0;
-  if (p.fwd_k[dl] != nullptr && hq == 0) {
-    const size_t dst_off = 2 * ((size_t)bb * NkT * p.Hkv * kD + (size_t)kvh * kD);
-    fw.kdst = (char*)p.fwd_k[dl] + dst_off;
-    fw.vdst = (char*)p.fwd_v[dl] + dst_off;
-    fw.t_lo = qt * (kBr / kBc);
-    fw.t_hi = min(fw.t_lo + kBr / kBc, lp.ntiles);
+  fw.v_lo = fw.v_hi = fw.v0 = fw.nk = 0;
+  if (p.fwd[dl] >= 0 && hq == 0) {
+    const int ref = p.fwd[dl];
+    const int64_t boff = (int64_t)(ref & 0xffff) * p.kv_block + (int64_t)kv_in_blk;
+    fw.kdst = p.kv_base[ref >> 16][0] + boff;
+    fw.vdst = p.kv_base[ref >> 16][1] + boff;
+    const bool two = nsub > 1;
+    fw.v0 = two ? cx.t0 : 0;
+    fw.nk = two ? cx.b1.nk : cx.b0.nk;
+    fw.v_lo = fw.v0 + qt * (kBr / kBc);
+    fw.v_hi = min(fw.v_lo + kBr / kBc, fw.v0 + (two ? cx.b1.ntiles : cx.b0.ntiles));
   }
   const int kswz = swz(j);
 #pragma unroll
@@ -486,11 +531,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   Softmax sm;
 
-  if (lp.ntiles > 0) {
+  if (cx.total > 0) {
     // prologue: the first kPrefetch tiles
 #pragma unroll
     for (int t = 0; t < kPrefetch; ++t)
-      if (t < lp.ntiles) {
+      if (t < cx.total) {
         const TileRequest r = make_request(cx, t, smem, t, wave);
 #pragma unroll
         for (int j = 0; j < 4; ++j) request_piece(r, j);
@@ -510,14 +555,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
     x_preload<0>(f, smem, ring);
     TileRequest req = make_request(cx, kPrefetch, smem, kPrefetch, wave);
     if (grp_b) __builtin_amdgcn_s_barrier();  // group B starts one window late
-    // positions 0 .. ntiles (the extra position drains the last P.V); tile t lives in stage t % 4
-    for (int t = 0; t <= lp.ntiles; t += kStages) {
+    // positions 0 .. total (the extra position drains the last P.V); virtual tile t lives in stage t % 4
+    for (int t = 0; t <= cx.total; t += kStages) {
       tile_windows<0>(cx, f, lp, smem, t, wave, ring, req, fw, s, pf, sm, o);
-      if (t + 1 > lp.ntiles) break;
+      if (t + 1 > cx.total) break;
       tile_windows<1>(cx, f, lp, smem, t + 1, wave, ring, req, fw, s, pf, sm, o);
-      if (t + 2 > lp.ntiles) break;
+      if (t + 2 > cx.total) break;
       tile_windows<2>(cx, f, lp, smem, t + 2, wave, ring, req, fw, s, pf, sm, o);
-      if (t + 3 > lp.ntiles) break;
+      if (t + 3 > cx.total) break;
       tile_windows<3>(cx, f, lp, smem, t + 3, wave, ring, req, fw, s, pf, sm, o);
     }
     if (!grp_b) __builtin_amdgcn_s_barrier();  // matches group B's extra barrier

@@ -68,6 +68,19 @@ def test_bf16_mfma_ring(gpu_lib, causal, layout, n):
     _check_ring(gpu_lib, 2, 4, n, 4, 2, 128, causal, layout, "bf16", 200 + n)
 
 
+@pytest.mark.parametrize("steps_per_launch", ["1", "2"])
+@pytest.mark.parametrize("P,n,causal,layout", [(5, 200, True, "contiguous"), (4, 320, True, "striped"),
+                                               (3, 128, False, "contiguous"), (4, 200, True, "zigzag"),
+                                               (7, 130, True, "striped"), (2, 257, True, "contiguous")])
+def test_bf16_ring_one_and_two_steps_per_launch(gpu_lib, monkeypatch, steps_per_launch, P, n, causal, layout):
+    """The whole local ring folds two ring steps per launch by default (the second block pulled from the
+    predecessor's slot, pushed on to the successor's next slot); RING_ATTN_STEPS_PER_LAUNCH=1 keeps one
+    step per launch.  Both match the oracle, with odd ring sizes (a last launch of one step) and ragged
+    blocks."""
+    monkeypatch.setenv("RING_ATTN_STEPS_PER_LAUNCH", steps_per_launch)
+    _check_ring(gpu_lib, 1, P, n, 4, 2, 128, causal, layout, "bf16", 270 + P * 10 + n)
+
+
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
 @pytest.mark.parametrize("n", [65, 257])
 def test_bf16_mfma_ring_query_tile_edges(gpu_lib, layout, n):
