@@ -8,11 +8,12 @@
 // a [M, K] (tokens x features, row-major), w [N, K] (the weight in nn.Linear layout: one row per
 // output feature), both read along k.
 //
-// A workgroup of 4 waves (one per SIMD, 256 accumulator registers each for 256 x 256 tiles) owns
-// BM x BN output tiles, one after the other (persistent: one workgroup per CU, or two with the
-// 128 x 128 tiles taken when the large ones would leave CUs idle); each wave a (BM/2) x (BN/2) quarter as
-// (BN/64) x (BM/64) accumulators of 32 x 32, held transposed (the lane is the token m, the register
-// the feature n, so that 4 consecutive features leave as one 8-byte store).  k advances in steps of
+// A workgroup owns BM x BN output tiles, one after the other (persistent): 256 x 256 tiles with 8
+// waves, two per SIMD, one workgroup per CU; or, when those would leave CUs idle, 128 x 128 tiles with
+// 4 waves and two workgroups per CU.  The waves form a (W/2) x 2 grid over the tile, each wave owning
+// (BM / (W/2)) x (BN/2) outputs as 32 x 32 accumulators (128 registers with 8 waves, so the 256 x 256
+// kernel holds everything in registers without spilling), held transposed (the lane is the token m,
+// the register the feature n, so that 4 consecutive features leave as one 8-byte store).  k advances in steps of
 // BK: the a and w rows of a step go HBM -> LDS directly (global_load_lds) into a ring of S buffers.
 // The steps of all of a workgroup's tiles form one stream: step s+S is requested into the buffer
 // of step s as soon as every wave has read it (one workgroup barrier per step), so S-1 steps are in
@@ -32,8 +33,6 @@ namespace {
 
 using namespace tile;
 
-constexpr int kFfnWaves = 4;
-constexpr int kFfnThreads = 64 * kFfnWaves;
 constexpr int kFfnGroupM = 4;  // m-tiles per sweep of the n-tiles
 // BM x BN output tiles, k steps of BK, S LDS buffers (2 x 64 KiB of the 160 KiB).  Deeper rings of
 // shorter steps (BK 32 with 4 or 5 buffers) measured no faster: the rate at which one CU pulls rows
@@ -67,8 +66,11 @@ __device__ __forceinline__ float activate(float z) {
   return z;
 }
 
-template <int BM, int BN, int BK, int S, int ACT, int OCC>
-__global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmParams p) {
+// W waves in a WM x WN grid (WM = W / 2 along m, WN = 2 along n); OCC workgroups per CU.
+template <int BM, int BN, int BK, int S, int ACT, int OCC, int W>
+__global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams p) {
+  constexpr int kFfnWaves = W;
+  constexpr int WN = 2, WM = W / WN;
   constexpr int R = BK * 2;                  // bytes of one row of a step
   constexpr int C = R / 16;                  // 16-byte chunks per row
   constexpr int RPP = 1024 / R;              // rows per 1 KiB copy
@@ -76,9 +78,9 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmP
   constexpr int kTileA = BM * R;
   constexpr int kStage = (BM + BN) * R;
   constexpr int kPieces = (BM + BN) / RPP / kFfnWaves;  // 1 KiB copies per wave per step
-  constexpr int MB = BM / 64, NB = BN / 64;             // 32 x 32 blocks per wave along m and n
+  constexpr int MB = BM / (32 * WM), NB = BN / (32 * WN);  // 32 x 32 blocks per wave along m and n
+  static_assert(MB >= 1 && NB >= 1 && MB * 32 * WM == BM && NB * 32 * WN == BN, "wave grid covers the tile");
   static_assert(R == 64 || R == 128, "step rows of 64 or 128 bytes");
-  static_assert(KK % 2 == 0, "fragment double buffer alternates per k slice");
   static_assert(kPieces * kFfnWaves * RPP == BM + BN, "tile rows split evenly over the waves");
   static_assert((S - 1) * kPieces < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * kStage];
@@ -114,32 +116,41 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmP
   // requests: piece q (0 .. (BM+BN)/RPP) holds tile rows RPP q .. + RPP-1 (a rows, then w rows);
   // lane l copies row RPP q + l / C, chunk (l % C) ^ swz(row) of the source to LDS chunk l % C.
   // Rows past the end of a and w re-read the last row.
+  // A piece covers RPP consecutive rows; its 16-byte chunk swizzle is the same for every piece of this
+  // wave (swz(row) depends on row / (256/R) mod C, and pieces of one wave start RPP * kFfnWaves rows
+  // apart, a multiple of 256/R * C), so one per-lane offset (lane's row within the piece and chunk)
+  // serves them all, with the piece's first row added as a scalar; only a piece that reaches past the
+  // last row of a or w takes the per-lane clamp.
+  static_assert((RPP * kFfnWaves) % ((256 / R) * C) == 0, "one chunk swizzle for all pieces of a wave");
   const char* xa = nullptr;
   const char* wa = nullptr;
-  uint32_t voff[kPieces];
+  int lim_a = 0, lim_w = 0;  // last valid row of this tile's a rows and w rows
+  const uint32_t lane_row = lane / C;
+  const uint32_t lane_chunk = ((lane % C) ^ swz(RPP * wave + lane / C)) * 16;
   int rq_tile = 0, rq_kt = 0;
   auto setup_request_tile = [&](int i) {
     int m0, n0;
     tile_of(i, m0, n0);
     xa = (const char*)p.x + (int64_t)m0 * p.ldx * 2;
     wa = (const char*)p.w + (int64_t)n0 * p.ldw * 2;
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      const int q = wave + kFfnWaves * k;
-      const int row = RPP * q + lane / C;
-      const int chunk = ((lane % C) ^ swz(row)) * 16;
-      if (RPP * q < BM) {
-        voff[k] = (uint32_t)(min(row, p.M - 1 - m0) * p.ldx * 2) + chunk;
-      } else {
-        voff[k] = (uint32_t)(min(row - BM, p.N - 1 - n0) * p.ldw * 2) + chunk;
-      }
-    }
+    lim_a = p.M - 1 - m0;
+    lim_w = p.N - 1 - n0;
   };
   // piece k of the requested step into buffer buf; then move the request on by one step
   auto issue_piece = [&](int k, int buf) {
     const int q = wave + kFfnWaves * k;
-    const bool is_a = kFfnWaves * k < BM / RPP;  // the same for every wave (wave < 4, BM/RPP % 4 == 0)
-    copy_to_lds16((is_a ? xa : wa) + rq_kt * R, voff[k], (uint32_t)(uintptr_t)(smem + buf * kStage) + q * 1024);
+    const bool is_a = kFfnWaves * k < BM / RPP;  // the same for every wave (wave < W, BM/RPP % W == 0)
+    const int row0 = RPP * q - (is_a ? 0 : BM);  // first row of the piece within the tile's a or w rows
+    const int lim = is_a ? lim_a : lim_w;
+    const int64_t ld2 = (is_a ? p.ldx : p.ldw) * 2;
+    const char* base = (is_a ? xa : wa) + rq_kt * R;
+    const uint32_t dst = (uint32_t)(uintptr_t)(smem + buf * kStage) + q * 1024;
+    if (row0 + RPP - 1 <= lim) {
+      copy_to_lds16(base + row0 * ld2, (uint32_t)(lane_row * ld2) + lane_chunk, dst);
+    } else {  // rows past the end re-read the last row
+      const int row = min(row0 + (int)lane_row, lim);
+      copy_to_lds16(base, (uint32_t)(row * ld2) + lane_chunk, dst);
+    }
   };
   auto advance_request = [&]() {
     if (++rq_kt == KT) {
@@ -152,41 +163,55 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmP
   int roff[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) roff[kk] = j * R + (((2 * kk + h2) ^ swz(j)) * 16);
-  const int wn = wave >> 1, wm = wave & 1;
-  const int a_row0 = wm * (BM / 2), w_row0 = kTileA / R + wn * (BN / 2);
+  const int wn = wave / WM, wm = wave % WM;
+  const int a_row0 = wm * (BM / WM), w_row0 = kTileA / R + wn * (BN / WN);
 
   f32x16 acc[NB][MB];
-  bf16x8 wf[2][NB], xf[2][MB];  // fragments of two k slices
-  // fragment r of k slice kk (r < NB: w rows of block r; else x rows of block r - NB) into `set`
-  auto read_one = [&](int buf, int kk, int set, int r) {
+  // one set of fragments: products run bn-major (product i = NB-block i / MB, MB-block i % MB), so
+  // w fragment bn of the next k slice is read right after product MB bn + MB - 1, its last use in the
+  // current slice, and x fragment bm after product (NB - 1) MB + bm; each read lands in the register
+  // its predecessor just freed, at least MB products before its first use
+  bf16x8 wf[NB], xf[MB];
+  // fragment r of k slice kk (r < NB: w rows of block r; else x rows of block r - NB)
+  auto read_one = [&](int buf, int kk, int r) {
     const LDS_AS char* base = smem + buf * kStage + roff[kk];
     if (r < NB)
-      wf[set][r] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (w_row0 + 32 * r) * R));
+      wf[r] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (w_row0 + 32 * r) * R));
     else
-      xf[set][r - NB] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (a_row0 + 32 * (r - NB)) * R));
+      xf[r - NB] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (a_row0 + 32 * (r - NB)) * R));
   };
-  auto mfma_one = [&](int set, int i) {
+  auto mfma_one = [&](int i) {
     const int bn = i / MB, bm = i % MB;
-    acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][bn], xf[set][bm], acc[bn][bm], 0, 0, 0);
+    acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[bn], xf[bm], acc[bn][bm], 0, 0, 0);
+  };
+  // the fragment reads that follow product i: those whose last use in the slice is product i
+  auto reads_after = [&](int i, int buf, int kk) {
+    if (i % MB == MB - 1) read_one(buf, kk, i / MB);            // w fragment bn = i / MB
+    if (i / MB == NB - 1) read_one(buf, kk, NB + i % MB);       // x fragment bm = i % MB
   };
 
   // epilogue of the tile at (m0, n0): register 4 g + e of block (bn, bm) is feature
-  // n = n0 + wn BN/2 + 32 bn + 8 g + 4 h2 + e of token m = m0 + wm BM/2 + 32 bm + j
+  // n = n0 + wn BN/WN + 32 bn + 8 g + 4 h2 + e of token m = m0 + wm BM/WM + 32 bm + j
   const unsigned short* bias = (const unsigned short*)p.bias;
   unsigned short* out = (unsigned short*)p.out;
-  auto epilogue = [&](int m0, int n0) {
+  // A tile that lies inside [0, M) x [0, N) stores without per-element bounds checks; only the edge
+  // tiles take the checked form (its branches would otherwise keep accumulator values live across
+  // every store and push the 256 x 256 kernel into scratch).
+  auto epilogue_body = [&](int m0, int n0, auto checked_tag) {
+    constexpr bool kChecked = decltype(checked_tag)::value;
 #pragma unroll
     for (int bn = 0; bn < NB; ++bn) {
-      const int nb = n0 + wn * (BN / 2) + 32 * bn + 4 * h2;
+      const int nb = n0 + wn * (BN / WN) + 32 * bn + 4 * h2;
       u16x4 bv[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = nb + 8 * g;
-        bv[g] = n < p.N ? *(const u16x4*)(bias + n) : u16x4{0, 0, 0, 0};
+        bv[g] = (!kChecked || n < p.N) ? *(const u16x4*)(bias + n) : u16x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int bm = 0; bm < MB; ++bm) {
-        const int m = m0 + wm * (BM / 2) + 32 * bm + j;
+        const int m = m0 + wm * (BM / WM) + 32 * bm + j;
+        unsigned short* orow = out + (int64_t)m * p.ldo;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = nb + 8 * g;
@@ -196,42 +221,44 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmP
             const float z = acc[bn][bm][4 * g + e] + __uint_as_float((uint32_t)bv[g][e] << 16);
             o[e] = __builtin_bit_cast(unsigned short, (__bf16)activate<ACT>(z));
           }
-          if (m < p.M && n < p.N) *(u16x4*)(out + (int64_t)m * p.ldo + n) = o;
+          if (!kChecked || (m < p.M && n < p.N)) *(u16x4*)(orow + n) = o;
         }
       }
     }
   };
+  auto epilogue = [&](int m0, int n0) {
+    if (m0 + BM <= p.M && n0 + BN <= p.N)
+      epilogue_body(m0, n0, std::false_type{});
+    else
+      epilogue_body(m0, n0, std::true_type{});
+  };
 
-  // One step: KK slices of NB x MB products.  Each product is followed by one slot of other work, in
-  // this order (sched_barrier keeps it): while slice kk multiplies, the fragments of slice kk+1 are
-  // read; the last slice first meets the other waves at the barrier (step s+1 landed, step s read by
-  // all), then reads step s+1's first fragments and requests step s+S into the freed buffer, so that
-  // the matrix cores keep running across the barrier and the copies.  Near the end of the stream the
-  // same schedule runs on: requests past the last step fetch the last tile's rows again into buffers
-  // that no step reads, and the fragments read for a step past the last one are not used.
+  // One step: KK slices of NB x MB products.  After each product come the fragment reads it frees
+  // (reads_after) and, in the last slice, the step's other work in fixed slots (sched_barrier keeps
+  // the order): product 0 first meets the other waves at the barrier (step s+1 landed, step s read by
+  // all: the next step's fragments are read from buffer (s+1) % S only after it), and the copies of
+  // step s+S into the freed buffer follow products 1 .. kProducts-1, so that the matrix cores keep
+  // running across the barrier and the copies.  Near the end of the stream the same schedule runs on:
+  // requests past the last step fetch the last tile's rows again into buffers that no step reads, and
+  // the fragments read for a step past the last one are not used.
   constexpr int kProducts = NB * MB;
-  constexpr int kReads = NB + MB;
-  static_assert(kProducts >= 4, "slots for the barrier, reads and copies");
+  static_assert(kProducts >= 4, "slots for the barrier and copies");
   auto step = [&](int s) {
     const int buf = s % S;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int set = kk & 1;
 #pragma unroll
       for (int i = 0; i < kProducts; ++i) {
-        mfma_one(set, i);
+        mfma_one(i);
         __builtin_amdgcn_sched_barrier(0);
         if (kk + 1 < KK) {
-#pragma unroll
-          for (int r = 0; r < kReads; ++r)
-            if (r % kProducts == i) read_one(buf, kk + 1, set ^ 1, r);
-        } else if (i == 0) {
-          wait_vmem<(S - 2) * kPieces>();  // step s+1 has landed (this wave's copies)
-          __syncthreads();                 // ... every wave's, and every wave has read all of step s
+          reads_after(i, buf, kk + 1);
         } else {
-#pragma unroll
-          for (int r = 0; r < kReads; ++r)
-            if (1 + r % (kProducts - 1) == i) read_one((s + 1) % S, 0, 0, r);
+          if (i == 0) {
+            wait_vmem<(S - 2) * kPieces>();  // step s+1 has landed (this wave's copies)
+            __syncthreads();                 // ... every wave's, and every wave has read all of step s
+          }
+          reads_after(i, (s + 1) % S, 0);
 #pragma unroll
           for (int k = 0; k < kPieces; ++k)
             if (1 + k * (kProducts - 1) / kPieces == i) issue_piece(k, buf);
@@ -252,7 +279,7 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_gemm_bf16(const FfnGemmP
   wait_vmem<(S - 1) * kPieces>();  // steps 1 .. S-1 may still fly
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kReads; ++r) read_one(0, 0, 0, r);
+  for (int r = 0; r < NB + MB; ++r) read_one(0, 0, r);
   for (int ti = 0; ti < nt; ++ti) {
 #pragma unroll
     for (int bn = 0; bn < NB; ++bn)
@@ -278,8 +305,9 @@ int cu_count() {
   return n;
 }
 
-// OCC workgroups per CU (1 for 256 x 256 tiles: 512 registers per lane; 2 for 128 x 128)
-template <int BM, int BN, int BK, int S, int ACT, int OCC>
+// OCC workgroups of W waves per CU: 256 x 256 tiles with 8 waves (two per SIMD, 64 x 128 outputs and
+// 128 accumulator registers each), 128 x 128 tiles with 4 waves and two workgroups per CU
+template <int BM, int BN, int BK, int S, int ACT, int OCC, int W>
 hipError_t launch_tiles(FfnGemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
@@ -288,7 +316,7 @@ hipError_t launch_tiles(FfnGemmParams p, hipStream_t stream) {
   // round of tiles keeps the XCD of each virtual index
   int G = std::min(T, OCC * cu_count());
   if (G < T) G = std::max(8, G / 8 * 8);
-  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, BK, S, ACT, OCC>), dim3(G), dim3(kFfnThreads), 0, stream, p);
+  hipLaunchKernelGGL((ffn_gemm_bf16<BM, BN, BK, S, ACT, OCC, W>), dim3(G), dim3(64 * W), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -297,8 +325,8 @@ hipError_t launch_tiles(FfnGemmParams p, hipStream_t stream) {
 template <int ACT>
 hipError_t launch_act(const FfnGemmParams& p, hipStream_t stream) {
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= cu_count()) return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, ACT, 1>(p, stream);
-  return launch_tiles<128, 128, kFfnBK, kFfnStages, ACT, 2>(p, stream);
+  if (big >= cu_count()) return launch_tiles<kFfnBM, kFfnBN, kFfnBK, kFfnStages, ACT, 1, 8>(p, stream);
+  return launch_tiles<128, 128, kFfnBK, kFfnStages, ACT, 2, 4>(p, stream);
 }
 
 }  // namespace
