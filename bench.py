@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s on 1 MI355X (causal & non-causal) + % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 CUS, BF16_FLOP_PER_CLK_PER_CU = 256, 4096  # dense bf16 MFMA rate per CU per clock
 
 
@@ -43,7 +44,7 @@ def clock_peak(sclk_mhz):
     return CUS * BF16_FLOP_PER_CLK_PER_CU * sclk_mhz * 1e6 / 1e12
 # the sources the forward step kernel is compiled from (its HBM traffic summary is tied to them)
 KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_step_amd", "csrc", f)
-                  for f in ("step_mfma_bf16.hip", "gfx950_tile.h", "internal.h")]
+                  for f in ("step_mfma_bf16.hip", "gfx950_tile.h", "step_params.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_mfma_bf16_d128.json")
 EVENT_EVERY = 4  # timed calls between two that carry per-step kernel events
 LAUNCH_MIN_MS = 0.02  # an event interval shorter than this holds no step kernel
@@ -99,7 +100,11 @@ def run_workload(w, steps, warmup, measure_clock=True):
     def up(x):
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
 
-    tq, tk, tv = up(qs), up(ks), up(vs)
+    def pinned(x):  # a new pinned host allocation holding x
+        return torch.from_numpy(x.view(np.int16)).pin_memory().view(torch.bfloat16)
+
+    tq = up(qs)
+    tk, tv = (pinned(ks), pinned(vs)) if w.kv_host else (up(ks), up(vs))
     del qs, ks, vs
     o = torch.empty_like(tq)
     lse = torch.empty((n_local, w.B, w.Hq, n), dtype=torch.float32, device="cuda")
@@ -251,6 +256,67 @@ def run_backward_workload(w, measure_clock=True):
     res = dict(workload=w.name, steps=steps, warmup=warmup, ms=ms, ms_median=per_call[len(per_call) // 2],
                ms_min=per_call[0], tflops=tflops, flops=flops, kernel_tflops=None, sclk_mhz=sclk, sclk_busy=busy)
     del tq, tk, tv, tdo, o, lse, dq, dk, dv, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_merge_workload(measure_clock=True):
+    """The merge phase of the non-causal 16k ring on its own (HBM-bound): one ``ring_attn_step`` that folds
+    a single 64-key tile into the running state of all 8 devices (it reads the queries and the fp32
+    state and writes the state back; the 64 keys add little compute) and the standalone
+    ``ring_attn_finalize`` (reads the state, writes the bf16 output and the log-sum-exp).  Achieved
+    GB/s = the algorithmic bytes of each call / its time, between HIP events over about 1 s of calls."""
+    import numpy as np
+    import torch
+
+    import blockwise_ring_attention_step_amd as ra
+    import synth_inputs as si
+
+    w = si.WORKLOADS["noncausal_16k"]
+    n_dev, B, H, N, D, NK = w.P, w.B, w.Hq, w.n, w.D, 64
+    q = torch.from_numpy(si.normal_bf16(w.seed, (n_dev, B, N, H, D)).view(np.int16)).view(torch.bfloat16).cuda()
+    k = torch.from_numpy(si.normal_bf16(w.seed + 1, (n_dev, B, NK, H, D)).view(np.int16)).view(torch.bfloat16).cuda()
+    v = torch.from_numpy(si.normal_bf16(w.seed + 2, (n_dev, B, NK, H, D)).view(np.int16)).view(torch.bfloat16).cuda()
+    o_acc = torch.zeros((n_dev, B, H, N, D), dtype=torch.float32, device="cuda")
+    m = torch.zeros((n_dev, B, H, N), dtype=torch.float32, device="cuda")
+    l = torch.zeros((n_dev, B, H, N), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((n_dev, B, H, N), dtype=torch.float32, device="cuda")
+    cs = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(D)
+    ra.ring_attn_step(q, k, v, o_acc, m, l, scale=scale, init=True, stream=cs)  # a valid state to continue
+
+    def fold():
+        ra.ring_attn_step(q, k, v, o_acc, m, l, scale=scale, stream=cs)
+
+    def fin():
+        ra.ring_attn_finalize(o_acc, m, l, o, lse, stream=cs)
+
+    rows = n_dev * B * H * N
+    bytes_fold = 2 * q.numel() + 2 * 2 * k.numel() + 2 * (rows * D * 4 + 2 * rows * 4)  # q, k, v, state in and out
+    bytes_fin = rows * D * 4 + 2 * rows * 4 + 2 * o.numel() + rows * 4                  # state in; o, lse out
+    res = {}
+    for name, fn, nbytes in (("fold", fold, bytes_fold), ("finalize", fin, bytes_fin)):
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        fn()
+        torch.cuda.synchronize()
+        steps = max(10, min(500, int(1.0 / max(time.time() - t1, 1e-5))))
+        ev = [ra.HipEvent() for _ in range(2)]
+        ev[0].record(cs)
+        for _ in range(steps):
+            fn()
+        ev[1].record(cs)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_ms(ev[1]) / steps
+        res[name] = dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+        log(f"merge phase, {name}: {ms * 1e3:.1f} us per call, {nbytes / 2**20:.1f} MiB, "
+            f"{res[name]['gbps']:.0f} GB/s ({100 * res[name]['gbps'] / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
+    del q, k, v, o_acc, m, l, o, lse
     torch.cuda.empty_cache()
     return res
 
@@ -460,6 +526,7 @@ def main():
                     help="untimed ring calls first; the GPU clock takes some tens of calls to settle")
     ap.add_argument("--workload", default="noncausal_16k")
     ap.add_argument("--extra", default="causal_striped_64k,causal_contig_64k,causal_zigzag_64k,causal_32k,causal_1m_shard,"
+                    "merge_phase_16k,"
                     "bwd_noncausal_16k,bwd_causal_striped_64k,bwd_causal_zigzag_64k,ffn_16k,ffn_32h_4k",
                     help="comma-separated extra workloads reported under 'extra' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -494,6 +561,15 @@ def main():
     main_res = run_workload(w, args.steps, args.warmup, not args.no_clock)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
+        if name == "merge_phase_16k":
+            r = run_merge_workload(not args.no_clock)
+            extras.append({"workload": name, "pass": "merge", "unit": "GB/s", "value": r["fold"]["gbps"],
+                           "ms_per_step": r["fold"]["ms"], "bytes_per_call": r["fold"]["bytes"],
+                           "frac_of_hbm_peak": r["fold"]["gbps"] / PEAK_HBM_GBPS,
+                           "finalize": {"ms": r["finalize"]["ms"], "bytes": r["finalize"]["bytes"],
+                                        "gbps": r["finalize"]["gbps"],
+                                        "frac_of_hbm_peak": r["finalize"]["gbps"] / PEAK_HBM_GBPS}})
+            continue
         if name in si.FFN_WORKLOADS:
             wf = si.FFN_WORKLOADS[name]
             r = run_ffn_workload(wf, not args.no_clock)

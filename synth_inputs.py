@@ -13,7 +13,8 @@ Workload recipes (token-major layout ``[B, S, H, D]``, as a sequence of tokens e
 * ``causal_32k``: B=1, S=32768, 32 heads, D=128, P=8 shards of 4096, N(0,1) scaled by 0.5, bf16.
 * ``causal_striped_64k``: B=1, S=65536, 32 query heads, 8 KV heads, D=128, P=8, N(0,1), bf16.
 * ``causal_1m_shard``: one device's share of a 1,048,576-token ring of 32 shards (n=32768):
-  local queries = the last shard, K/V = the whole sequence, 8 heads, D=128, N(0,1), bf16.
+  local queries = the last shard, K/V = the whole sequence, 8 heads, D=128, N(0,1), bf16;
+  ``causal_1m_shard_host`` the same with the key/value source in pinned host memory.
 
 Feed-forward workloads (the blockwise feed-forward after attention; the pages give no sizes, so
 d_model = Hq * D of an attention workload and d_ff = 4 d_model): x ~ N(0, 1) (an attention output
@@ -53,6 +54,8 @@ class Workload:
     local_shard: int | None = None
     # the backward ring (gradients for a seeded output gradient) instead of the forward
     backward: bool = False
+    # key/value source in pinned host memory instead of HBM (every hop a host-to-device copy)
+    kv_host: bool = False
 
     @property
     def n(self) -> int:
@@ -82,6 +85,8 @@ WORKLOADS = {
     "causal_zigzag_64k": Workload("causal_zigzag_64k", 1, 65536, 8, 32, 8, 128, True, "zigzag", "bf16", 4000),
     "causal_1m_shard": Workload("causal_1m_shard", 1, 1048576, 32, 8, 8, 128, True, "contiguous", "bf16", 5000,
                                 local_shard=31),
+    "causal_1m_shard_host": Workload("causal_1m_shard_host", 1, 1048576, 32, 8, 8, 128, True, "contiguous", "bf16",
+                                     5000, local_shard=31, kv_host=True),
     "bwd_noncausal_16k": Workload("bwd_noncausal_16k", 1, 16384, 8, 8, 8, 128, False, "contiguous", "bf16", 2000,
                                   backward=True),
     "bwd_causal_striped_64k": Workload("bwd_causal_striped_64k", 1, 65536, 8, 32, 8, 128, True, "striped", "bf16",

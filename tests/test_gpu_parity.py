@@ -380,6 +380,35 @@ def test_state_snapshot_and_resume(gpu_lib):
     assert max_err(unshard_lse(res[0][1], "contiguous"), ref_lse) <= TOL_BF16_LSE
 
 
+@pytest.mark.parametrize("D,dtype", [(5, "f32"), (5, "bf16"), (128, "bf16"), (128, "f32"), (12, "bf16")])
+def test_finalize_divides_and_writes_lse(gpu_lib, D, dtype):
+    """ring_attn_finalize on a random valid state (the vector kernel for D % 4 == 0, the scalar one
+    otherwise): o = o_acc / l in token-major order, lse = (m + log2 l) ln 2, and o = 0, lse = -inf
+    where l = 0; checked against the same formulas in float64."""
+    ra = gpu_lib
+    n_dev, B, Hq, Nq = 3, 2, 5, 37
+    rng = np.random.default_rng(1800 + D)
+    o_acc = rng.standard_normal((n_dev, B, Hq, Nq, D)).astype(np.float32) * 4
+    m = rng.standard_normal((n_dev, B, Hq, Nq)).astype(np.float32) * 10
+    l = rng.uniform(1, 100, (n_dev, B, Hq, Nq)).astype(np.float32)
+    empty = rng.random((n_dev, B, Hq, Nq)) < 0.1
+    l[empty] = 0
+    o_acc[empty] = 0
+    m[empty] = -np.inf
+    t = [torch.from_numpy(x).cuda() for x in (o_acc, m, l)]
+    o = torch.empty((n_dev, B, Nq, Hq, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    lse = torch.empty((n_dev, B, Hq, Nq), dtype=torch.float32, device="cuda")
+    ra.ring_attn_finalize(*t, o, lse)
+    torch.cuda.synchronize()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        want_o = np.where(l[..., None] > 0, o_acc.astype(np.float64) / l[..., None], 0.0).transpose(0, 1, 3, 2, 4)
+        want_l = np.where(l > 0, (m.astype(np.float64) + np.log2(l.astype(np.float64))) * math.log(2.0), -np.inf)
+    got_o = o.float().cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -8 * np.abs(want_o).max() if dtype == "bf16" else 1e-6 * np.abs(want_o).max()
+    assert max_err(got_o, want_o) <= tol
+    assert max_err(lse.cpu().numpy(), want_l) <= 1e-5 * np.abs(want_l[np.isfinite(want_l)]).max()
+
+
 def test_empty_and_fully_masked_edges(gpu_lib):
     ra = gpu_lib
     D, Hq = 128, 2
