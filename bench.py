@@ -78,7 +78,7 @@ def shard_np(x, P, layout):
     return np.ascontiguousarray(y)
 
 
-def run_workload(w, steps, warmup, measure_clock=True):
+def run_workload(w, steps, warmup, measure_clock=True, inputs="normal"):
     import numpy as np
     import torch
 
@@ -87,6 +87,9 @@ def run_workload(w, steps, warmup, measure_clock=True):
 
     t0 = time.time()
     q, k, v = si.workload_qkv(w)
+    if inputs == "constant":  # every element 1.0: the same instruction stream with no operand bit activity
+        for x in (q, k, v):
+            x.fill(0x3F80)
     n = w.n
     if w.local_shard is None:
         qs = shard_np(q, w.P, w.layout)
@@ -532,6 +535,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the amdsmi clock reading")
+    ap.add_argument("--inputs", choices=["normal", "constant"], default="normal",
+                    help="'constant' sets every q, k, v element of the main workload to 1.0: a diagnostic of how "
+                         "the clock depends on operand bit activity (the kernels execute the same instructions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -558,7 +564,7 @@ def main():
         log("copied 3 x 1 GiB")
         return
     w = si.WORKLOADS[args.workload]
-    main_res = run_workload(w, args.steps, args.warmup, not args.no_clock)
+    main_res = run_workload(w, args.steps, args.warmup, not args.no_clock, args.inputs)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
         if name == "merge_phase_16k":
@@ -610,7 +616,9 @@ def main():
     line = {
         "metric": METRIC, "value": main_res["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": main_res["ms"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": ("synthetic (seeded N(0,1), bf16)" if args.inputs == "normal" else
+                 "constant 1.0 (clock diagnostic, not the benchmark input)"),
         "config": {"workload": w.name, "B": w.B, "S": w.S, "P": w.P, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "mask": "causal" if w.causal else "none", "layout": w.layout,
                    "steps_per_launch": 2,
