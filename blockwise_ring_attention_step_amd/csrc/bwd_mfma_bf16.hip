@@ -115,6 +115,38 @@ __device__ __forceinline__ bf16x8 pack_half(const float (&x)[16], int h) {
   return r;
 }
 
+// A stream of N products whose A operands are read from LDS: operand I is read KA positions before
+// its product into a small ring of registers, and scheduling barriers keep that order, so the LDS
+// latency hides behind the products in flight instead of stalling each one.  op(ic) reads operand I,
+// prod(ic, a) issues product I (ic = std::integral_constant<int, I>).  stream_preload reads the
+// first KA operands, which lets a caller start those reads early (before a barrier, or before
+// arithmetic that the stream's B operands wait for).
+template <int KA>
+struct OperandRing {
+  bf16x8 r[KA + 2];
+};
+
+template <int N, int KA, int I = 0, typename Op>
+__device__ __forceinline__ void stream_preload(OperandRing<KA>& ring, const Op& op) {
+  if constexpr (I < KA && I < N) {
+    ring.r[I] = op(std::integral_constant<int, I>{});
+    stream_preload<N, KA, I + 1>(ring, op);
+  }
+}
+
+template <int N, int KA, int I = 0, typename Op, typename Prod>
+__device__ __forceinline__ void stream_run(OperandRing<KA>& ring, const Op& op, const Prod& prod) {
+  if constexpr (I < N) {
+    if constexpr (I + KA < N) ring.r[(I + KA) % (KA + 2)] = op(std::integral_constant<int, I + KA>{});
+    __builtin_amdgcn_sched_barrier(0);
+    prod(std::integral_constant<int, I>{}, ring.r[I % (KA + 2)]);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_run<N, KA, I + 1>(ring, op, prod);
+  }
+}
+
+constexpr int kAheadBwd = 3;  // operand reads in flight ahead of the products
+
 // ------------------------------------------------------------------------------------------------
 // bwd_dq: 256 query rows per workgroup, 8 waves (two per SIMD).
 constexpr int kDqWaves = 8;
@@ -219,44 +251,61 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   // per-lane base plus an immediate
   auto tile = [&](auto stage_tag, int t) {
     constexpr int ST = decltype(stage_tag)::value;
-    if (t + 2 < ntiles) dq_request(cx, t + 2, (ST + 2) % kBwdStages, smem);
+    const LDS_AS char* kt = smem + ST * kTileBytes;
     const int key0 = t * kTile;
-    if (key0 <= kmax_wave) {  // else no row of this wave sees the tile
-      const LDS_AS char* kt = smem + ST * kTileBytes;
-      const LDS_AS char* vt = kt + kDqVRing;
-      const bool masked = key0 + kTile - 1 > kmin_wave;
+    const bool work = key0 <= kmax_wave;  // else no row of this wave sees the tile
+    const bool masked = key0 + kTile - 1 > kmin_wave;
+    // per 32-key half cc: 16 products S^T / dP^T (even / odd items, k step item / 2; A = K / V rows),
+    // then 8 products dQ^T += K^T dS^T (16-key block 2 cc + item / 4, d tile item % 4)
+    auto op_sd = [&](auto ccc) {
+      return [&, ccc](auto ic) {
+        constexpr int CC = decltype(ccc)::value, I = decltype(ic)::value;
+        return read_rows(kt + (I & 1) * kDqVRing, CC, to.rowoff[I >> 1]);
+      };
+    };
+    auto op_dq = [&](auto ccc) {
+      return [&, ccc](auto ic) {
+        constexpr int CC = decltype(ccc)::value, I = decltype(ic)::value;
+        return read_transposed(kt, 2 * CC + (I >> 2), to, I & 3);
+      };
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    OperandRing<kAheadBwd> rsd;
+    if (work) stream_preload<16, kAheadBwd>(rsd, op_sd(C0{}));
+    if (t + 2 < ntiles) dq_request(cx, t + 2, (ST + 2) % kBwdStages, smem);
+    auto half = [&](auto ccc) {
+      constexpr int CC = decltype(ccc)::value;
+      f32x16 sd[2] = {f32x16{}, f32x16{}};  // S^T, dP^T
+      stream_run<16, kAheadBwd>(rsd, op_sd(ccc), [&](auto ic, bf16x8 a) {
+        constexpr int I = decltype(ic)::value;
+        sd[I & 1] = mfma(a, (I & 1) ? df[I >> 1] : qf[I >> 1], sd[I & 1]);
+      });
+      // the dQ operands, and the next half's first score operands, are read before the arithmetic
+      OperandRing<kAheadBwd> rq;
+      stream_preload<8, kAheadBwd>(rq, op_dq(ccc));
+      if constexpr (CC == 0) stream_preload<16, kAheadBwd>(rsd, op_sd(C1{}));
+      float pr[16], ds[16];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        f32x16 s = {}, dp = {};
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], c, -lse2));
+      if (masked) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          s = mfma(read_rows(kt, cc, to.rowoff[kk]), qf[kk], s);
-          dp = mfma(read_rows(vt, cc, to.rowoff[kk]), df[kk], dp);
-        }
-        float pr[16], ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        if (masked) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * cc + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (key > kmax_lane) pr[r] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dp[r] - delta);
-        const bf16x8 b0 = pack_half(ds, 0), b1 = pack_half(ds, 1);
-        bf16x8 ta[3];
-        ta[0] = read_transposed(kt, 2 * cc, to, 0);
-        ta[1] = read_transposed(kt, 2 * cc, to, 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {  // item i: 16-key block 2 cc + i / 4, d tile i % 4
-          if (i + 2 < 8) ta[(i + 2) % 3] = read_transposed(kt, 2 * cc + (i + 2) / 4, to, (i + 2) % 4);
-          __builtin_amdgcn_sched_barrier(0);
-          dqt[i % 4] = mfma(ta[i % 3], i < 4 ? b0 : b1, dqt[i % 4]);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * CC + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (key > kmax_lane) pr[r] = 0.f;
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (sd[1][r] - delta);
+      const bf16x8 b0 = pack_half(ds, 0), b1 = pack_half(ds, 1);
+      stream_run<8, kAheadBwd>(rq, op_dq(ccc), [&](auto ic, bf16x8 a) {
+        constexpr int I = decltype(ic)::value;
+        dqt[I & 3] = mfma(a, I < 4 ? b0 : b1, dqt[I & 3]);
+      });
+    };
+    if (work) {
+      half(C0{});
+      half(C1{});
     }
     if (t + 1 < ntiles) {
       if (t + 2 < ntiles)
@@ -425,14 +474,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
     __syncthreads();
   }
   constexpr int kPerRequest = 2 * kKvPieces + 1;  // vector-memory instructions per wave per request
+  // this wave's first-half operand rows: Q rows (value wave) or dO rows (key wave) of a stage
+  int rowoff_w[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) rowoff_w[kk] = to.rowoff[kk] + (key_wave ? kTileBytes : 0);
   // one query tile (item it, LDS stage ST = it % 3); unrolled by three below so that every LDS
   // address is a per-lane base plus an immediate
   auto tile = [&](auto stage_tag, int it) {
     constexpr int ST = decltype(stage_tag)::value;
-    if (it + 2 < nitems) {
-      kv_request(cx, (ST + 2) % kBwdStages, rhq, rqt, smem);
-      advance(rhq, rqt);
-    }
     const int q0 = qt * kTile;
     qt = qt + 1 == nqt ? qt_first : qt + 1;
     const bool work = q0 + kTile > qmin_wave;  // else no key of this wave (pair) is seen by the tile's rows
@@ -442,61 +491,64 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
     const LDS_AS float* lsel = (const LDS_AS float*)(st + 2 * kTileBytes);
     const LDS_AS float* dell = lsel + kTile;
     const bool masked = q0 < qmax_wave || q0 + kTile > Nq;
-    // first half: P (value wave) or dP (key wave) of the two 32-row halves, in the same registers
+    // first half: S = Q K^T (value wave) or dP = dO V^T (key wave) of the two 32-row halves; the
+    // products alternate halves (two accumulator chains)
+    auto op1 = [&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      return read_rows(st, I & 1, rowoff_w[I >> 1]);
+    };
+    OperandRing<kAheadBwd> ring;
+    if (work) stream_preload<16, kAheadBwd>(ring, op1);
+    if (it + 2 < nitems) {
+      kv_request(cx, (ST + 2) % kBwdStages, rhq, rqt, smem);
+      advance(rhq, rqt);
+    }
     f32x16 t2[2];
+    bf16x8 pk[2][2];  // value wave: P in bf16, the B operands of dV^T += dO^T P
     if (work) {
+      t2[0] = f32x16{};
+      t2[1] = f32x16{};
+      stream_run<16, kAheadBwd>(ring, op1, [&](auto ic, bf16x8 a) {
+        constexpr int I = decltype(ic)::value;
+        t2[I & 1] = mfma(a, kvf[I >> 1], t2[I & 1]);
+      });
       if (!key_wave) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          f32x16 sc = {};
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) sc = mfma(read_rows(qtl, c2, to.rowoff[kk]), kvf[kk], sc);
           // row of register r: 32 c2 + 8 (r / 4) + 4 h2 + r % 4
           f32x4 l4[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) l4[g] = *(const LDS_AS f32x4*)(lsel + 32 * c2 + 8 * g + 4 * h2);
+          float x[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t2[c2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l4[r >> 2][r & 3]));
+          for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(t2[c2][r], c, -l4[r >> 2][r & 3]));
           if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int row = q0 + 32 * c2 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-              if (row < qmin_lane || row >= Nq) t2[c2][r] = 0.f;
+              if (row < qmin_lane || row >= Nq) x[r] = 0.f;
             }
           }
-          float x[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = t2[c2][r];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) pbuf[(2 * c2 + hh) * 64 + lane] = __builtin_bit_cast(i16x8, pack_half(x, hh));
-        }
-      } else {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          t2[c2] = f32x16{};
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) t2[c2] = mfma(read_rows(dtl, c2, to.rowoff[kk]), kvf[kk], t2[c2]);
+          for (int hh = 0; hh < 2; ++hh) {
+            pk[c2][hh] = pack_half(x, hh);
+            pbuf[(2 * c2 + hh) * 64 + lane] = __builtin_bit_cast(i16x8, pk[c2][hh]);
+          }
         }
       }
     }
+    // second half's first operands (dO^T or Q^T of this tile, resident since the tile's barrier)
+    // are read before the barrier, whose wait hides their latency
+    auto op2 = [&](auto ic) {
+      constexpr int I = decltype(ic)::value;  // 16-row block 2 c2 + hh = I / 4, d tile I % 4
+      return read_transposed(key_wave ? qtl : dtl, I >> 2, to, I & 3);
+    };
+    OperandRing<kAheadBwd> ring2;
+    if (work) stream_preload<16, kAheadBwd>(ring2, op2);
     __syncthreads();  // P of this tile is in LDS
     // second half: dV^T += dO^T P (value wave) or dS = P (dP - delta), dK^T += Q^T dS (key wave)
     if (work) {
-      if (!key_wave) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          float x[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = t2[c2][r];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bf16x8 b = pack_half(x, hh);
-            __builtin_amdgcn_sched_barrier(0);  // bounds how far the scheduler hoists operand reads
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(read_transposed(dtl, 2 * c2 + hh, to, dt), b, acc[dt]);
-          }
-        }
-      } else {
+      if (key_wave) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           float x[16];
@@ -512,14 +564,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
             }
           }
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bf16x8 b = pack_half(x, hh);
-            __builtin_amdgcn_sched_barrier(0);  // bounds how far the scheduler hoists operand reads
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(read_transposed(qtl, 2 * c2 + hh, to, dt), b, acc[dt]);
-          }
+          for (int hh = 0; hh < 2; ++hh) pk[c2][hh] = pack_half(x, hh);
         }
       }
+      stream_run<16, kAheadBwd>(ring2, op2, [&](auto ic, bf16x8 a) {
+        constexpr int I = decltype(ic)::value;
+        acc[I & 3] = mfma(a, pk[I >> 3][(I >> 2) & 1], acc[I & 3]);
+      });
     }
     if (it + 1 < nitems) {
       if (it + 2 < nitems)
