@@ -242,11 +242,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dqt[dt] = f32x16{};
 
-  if (ntiles > 0) {
+  if (ntiles > 0)
     for (int t = 0; t < 2 && t < ntiles; ++t) dq_request(cx, t, t, smem);
-    wait_vmem<0>();
-    __syncthreads();
-  }
+  // on every path into the loop (see bwd_dkv): the Q^T / dO^T fragment loads are complete
+  wait_vmem<0>();
+  __syncthreads();
   // one key tile (t, LDS stage ST = t % 3); unrolled by three below so that every LDS address is a
   // per-lane base plus an immediate
   auto tile = [&](auto stage_tag, int t) {
@@ -470,9 +470,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
       kv_request(cx, it, rhq, rqt, smem);
       advance(rhq, rqt);
     }
-    wait_vmem<0>();
-    __syncthreads();
   }
+  // on every path into the loop, including the empty one: the compiler's wait bookkeeping then knows
+  // that the K^T / V^T fragment loads are complete, and puts no vmcnt wait in front of their uses in
+  // the loop (one there would also wait for each tile request just issued)
+  wait_vmem<0>();
+  __syncthreads();
   constexpr int kPerRequest = 2 * kKvPieces + 1;  // vector-memory instructions per wave per request
   // this wave's first-half operand rows: Q rows (value wave) or dO rows (key wave) of a stage
   int rowoff_w[8];
