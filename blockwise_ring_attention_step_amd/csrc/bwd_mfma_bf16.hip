@@ -258,13 +258,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
     // per 32-key half cc: 16 products S^T / dP^T (even / odd items, k step item / 2; A = K / V rows),
     // then 8 products dQ^T += K^T dS^T (16-key block 2 cc + item / 4, d tile item % 4)
     auto op_sd = [&](auto ccc) {
-      return [&, ccc](auto ic) {
+      return [&](auto ic) {
         constexpr int CC = decltype(ccc)::value, I = decltype(ic)::value;
         return read_rows(kt + (I & 1) * kDqVRing, CC, to.rowoff[I >> 1]);
       };
     };
     auto op_dq = [&](auto ccc) {
-      return [&, ccc](auto ic) {
+      return [&](auto ic) {
         constexpr int CC = decltype(ccc)::value, I = decltype(ic)::value;
         return read_transposed(kt, 2 * CC + (I >> 2), to, I & 3);
       };
