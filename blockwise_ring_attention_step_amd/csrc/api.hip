@@ -1073,6 +1073,7 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
     p.k_off[x] = ko;
     p.flags[x] = (uint8_t)(((flags & RA_BWD_INIT_DQ) ? ra::kBwdInitDq : 0) |
                            ((flags & RA_BWD_INIT_DKV) ? ra::kBwdInitDkv : 0));
+    p.fwd[x] = -1;  // a single step hands nothing on
   }
   if (p.n_launch == 0) return RA_OK;
   rc = hip_status(launch_bwd(p, dtype, true, st));
@@ -1198,14 +1199,48 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   }
   const char* ksrc = (const char*)k_src;
   const char* vsrc = (const char*)v_src;
-  // the blocks of step s >= 1 arrive by copy into staging slot s & 1 (block (i - s) mod P of every
-  // local device, copied from its source shard); step 0 reads each device's own shard in place
+  // Hop plan, as in the forward: with the bf16 D=128 kernels a device that computes at step s hands its
+  // block to its local successor inside the step-s bwd_dq kernel (the rows it stages in LDS are stored
+  // into the successor's part of slot (s+1) & 1), where every forwarded row is staged by its workgroup.
+  // fwd_to[s*n_local+t]: successor fed by device t's step-s kernel (-1: none); by_kernel[s*n_local+t]:
+  // device t's step-s block arrives that way.
+  const bool in_step_hop = uses_mfma_kernel(dtype, D) && nh == 1;
+  std::vector<int> fwd_to((size_t)P * n_local, -1);
+  std::vector<uint8_t> by_kernel((size_t)P * n_local, 0);
+  if (in_step_hop) {
+    const int64_t st = layout_stride(layout, P);
+    for (int s = 0; s + 1 < P; ++s)
+      for (int t = 0; t < n_local; ++t) {
+        if (cls[(size_t)s * n_units + t] == 0) continue;
+        const int succ = t + 1 < n_local ? t + 1 : (n_local == P ? 0 : -1);
+        if (succ < 0) continue;
+        const int i = dev0 + t, j = ((i - s) % P + P) % P;
+        if (!step_forward_covers(causal, block_offset(layout, P, n, i), st, n, block_offset(layout, P, n, j), st, n))
+          continue;
+        fwd_to[(size_t)s * n_local + t] = succ;
+        by_kernel[(size_t)(s + 1) * n_local + succ] = 1;
+      }
+  }
+  auto needs_copy = [&](int s) -> bool {  // step s >= 1 has a block that no kernel hands over
+    if (s < 1 || s >= P) return false;
+    for (int t = 0; t < n_local; ++t)
+      if (!by_kernel[(size_t)s * n_local + t]) return true;
+    return false;
+  };
+  // the blocks of step s >= 1 not handed over by a kernel arrive by copy into staging slot s & 1 (block
+  // (i - s) mod P of the local device, copied from its source shard); step 0 reads each device's own
+  // shard in place
   auto enqueue_hop = [&](int s) -> hipError_t {
     const int sl = s & 1;
     for (int t = 0; t < n_local;) {
+      if (by_kernel[(size_t)s * n_local + t]) {
+        ++t;
+        continue;
+      }
       const int j0 = ((dev0 + t - s) % P + P) % P;
       int t2 = t + 1;
-      while (t2 < n_local && ((dev0 + t2 - s) % P + P) % P == j0 + (t2 - t)) ++t2;  // contiguous source run
+      while (t2 < n_local && !by_kernel[(size_t)s * n_local + t2] && ((dev0 + t2 - s) % P + P) % P == j0 + (t2 - t))
+        ++t2;  // contiguous source run
       const size_t bytes = (size_t)(t2 - t) * blk;
       hipError_t e = poison(hs, stage_k[sl] + t * blk, bytes, xs);
       if (e == hipSuccess) e = poison(hs, stage_v[sl] + t * blk, bytes, xs);
@@ -1225,13 +1260,13 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
     RA_CHECK(ra::launch_zero_f32(dv, dkv_bytes / 4, cs));
   }
   for (int s = 0; s < P; ++s) {
-    if (s + 1 < P) {  // copies for step s+1, into the slot that step s-1 read
+    if (needs_copy(s + 1)) {  // copies for step s+1, into the slot that step s-1 read
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
       RA_CHECK(jitter(hs.jitter_copy, xs));
       RA_CHECK(enqueue_hop(s + 1));
       RA_CHECK(hipEventRecord(ev_copy[(s + 1) & 1], xs));
     }
-    if (s >= 1) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
+    if (needs_copy(s)) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[s & 1], 0));
     ra::BwdParams p{};
     p.q = q_local;
     p.k = s > 0 ? (const void*)stage_k[s & 1] : (const void*)(ksrc + (size_t)dev0 * blk);
@@ -1242,6 +1277,8 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
     p.dq = dq_local;
     p.dk = dk;
     p.dv = dv;
+    p.fwd_k = stage_k[(s + 1) & 1];
+    p.fwd_v = stage_v[(s + 1) & 1];
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -1276,6 +1313,13 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
           p.q_stride = un.stride;  // the same for every unit of a layout
           p.k_stride = un.stride;
           p.flags[x] = first_flags[(size_t)s * n_units + u];
+          const int succ = dq_pass && in_step_hop ? fwd_to[(size_t)s * n_local + t] : -1;
+          p.fwd[x] = succ;
+          if (succ >= 0) {  // the slot this kernel fills was last read by step s-1, earlier on this stream
+            hipError_t e = poison(hs, stage_k[(s + 1) & 1] + (size_t)succ * blk, blk, cs);
+            if (e == hipSuccess) e = poison(hs, stage_v[(s + 1) & 1] + (size_t)succ * blk, blk, cs);
+            if (e != hipSuccess) return e;
+          }
         }
         const hipError_t e = launch_bwd(p, dtype, dq_pass, cs);
         if (e != hipSuccess) return e;
@@ -1290,7 +1334,7 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
       RA_CHECK(launch_units(0, false));
       RA_CHECK(launch_units(1, false));
     }
-    if (s + 2 < P) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
+    if (needs_copy(s + 2)) RA_CHECK(hipEventRecord(ev_comp[s & 1], cs));
   }
   // gradients nothing contributed to: zero (a zigzag unit always sees its own block's keys)
   const size_t qn = (size_t)B * n * Hq * D, kn = (size_t)B * n * Hkv * D;

@@ -162,6 +162,30 @@ struct DqCtx {
   int wave;
 };
 
+// The ring hop inside bwd_dq: the rows of tile t this wave copied into LDS stage `stage` (K and V), stored
+// back to the same offsets of the destination block (the successor's receive slot).  Each lane stores the
+// 16 bytes it copied itself, so its own vmcnt wait for the copy is all the ordering needed; rows past the
+// end of a ragged block are not stored.
+__device__ __forceinline__ void dq_forward(const DqCtx& cx, char* kdst, char* vdst, int t, int stage,
+                                           const LDS_AS char* smem) {
+  const int lane = __lane_id();
+  const int key0 = t * kTile;
+  const int64_t tofs = (int64_t)key0 * cx.k.row_bytes;
+#pragma unroll
+  for (int i = 0; i < kDqPieces; ++i) {
+    const int piece = cx.wave * kDqPieces + i;
+    const int row = piece * 4 + (lane >> 4);
+    const LDS_AS char* src = smem + stage * kTileBytes + piece * 1024 + 16 * lane;
+    const i16x8 kd = *(const LDS_AS i16x8*)src;
+    const i16x8 vd = *(const LDS_AS i16x8*)(src + kDqVRing);
+    if (key0 + row < cx.nk) {
+      const int64_t off = tofs + (int64_t)row * cx.k.row_bytes + ((lane & 15) ^ swz(row)) * 16;
+      *(i16x8*)(kdst + off) = kd;
+      *(i16x8*)(vdst + off) = vd;
+    }
+  }
+}
+
 __device__ __forceinline__ void dq_request(const DqCtx& cx, int t, int stage, const LDS_AS char* smem) {
   TileSrc k = cx.k, v = cx.v;
   k.base += t * cx.tile_stride;
@@ -237,6 +261,19 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   cx.nk = nk;
   cx.wave = wave;
   const TileOffsets to = tile_offsets();
+  // the hop inside the step: the workgroups of the first query head of each key/value head hand the
+  // block on to the successor's receive slot, each the 256 keys that line up with its query tile
+  // (tiles [fw_lo, fw_hi) of the block, all of which it loads)
+  char* fw_k = nullptr;
+  char* fw_v = nullptr;
+  int fw_lo = 0, fw_hi = 0;
+  if (p.fwd[dl] >= 0 && hq == 0 && p.fwd_k && p.fwd_v) {
+    const size_t fw_off = 2 * ((((size_t)p.fwd[dl] * p.B + bb) * p.NkTot) * p.Hkv * kD + (size_t)kvh * kD);
+    fw_k = (char*)p.fwd_k + fw_off;
+    fw_v = (char*)p.fwd_v + fw_off;
+    fw_lo = qt * (kDqRows / kTile);
+    fw_hi = min(fw_lo + kDqRows / kTile, ntiles);
+  }
 
   f32x16 dqt[4];
 #pragma unroll
@@ -273,6 +310,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
     using C1 = std::integral_constant<int, 1>;
     OperandRing<kAheadBwd> rsd;
     if (work) stream_preload<16, kAheadBwd>(rsd, op_sd(C0{}));
+    // the hop's stores go out before this tile's request, so that the wait at the tile's end (all but
+    // the latest request) also covers them and the vmcnt counts stay those of the copies
+    if (t >= fw_lo && t < fw_hi) dq_forward(cx, fw_k, fw_v, t, ST, smem);
     if (t + 2 < ntiles) dq_request(cx, t + 2, (ST + 2) % kBwdStages, smem);
     auto half = [&](auto ccc) {
       constexpr int CC = decltype(ccc)::value;

@@ -31,6 +31,8 @@ struct BwdParams {
   float* dq;           // [.., B, NqTot, Hq, D] fp32
   float* dk;           // [.., B, NkTot, Hkv, D] fp32
   float* dv;
+  void* fwd_k;         // the next step's receive slot (like k), filled by bwd_dq where fwd[t] >= 0
+  void* fwd_v;
   int n_launch;
   int B, Hq, Hkv, Nq, Nk, NqTot, NkTot, D;  // Nq: query rows per slot; Nk: the largest nk[t]
   int causal;
@@ -45,6 +47,7 @@ struct BwdParams {
   int64_t q_off[RA_MAX_DEV];
   int64_t k_off[RA_MAX_DEV];
   uint8_t flags[RA_MAX_DEV];
+  int fwd[RA_MAX_DEV];  // bwd_dq: device position in fwd_k / fwd_v that slot t's block is handed to, or -1
 };
 
 // One projection of the blockwise feed-forward: out[m, n] = act(sum_k x[m, k] w[n, k] + bias[n]) in

@@ -2,7 +2,8 @@
 
 The hop that "Ring Attention Là Gì?" (thienlv.com, section "Ring Attention Hoạt Động Thế Nào?")
 describes, the next block in flight while the current one is used, is emulated with two receive
-slots per device: copies on a second stream, or stores from inside the step kernel.  A slot that is
+slots per device: copies on a second stream, or stores from inside the step kernel (the forward step
+kernel, and the backward's query-gradient kernel).  A slot that is
 read before its block has landed, or overwritten while still being read, gives wrong results only
 under some timings, so the library's test hooks (RING_ATTN_HOP_STRESS, documented in ring_attn.h)
 change the timing and make stale data visible:
@@ -82,7 +83,7 @@ def test_forward_ring_unchanged_under_hop_stress(gpu_lib, monkeypatch, case):
     monkeypatch.delenv("RING_ATTN_HOP_STRESS", raising=False)
 
 
-@pytest.mark.parametrize("layout", ["striped", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 def test_backward_ring_unchanged_under_hop_stress(gpu_lib, monkeypatch, layout):
     ra = gpu_lib
     P, n, Hq, Hkv, D = 4, 256, 4, 2, 128
