@@ -307,10 +307,14 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
  *            device run as two units, as in ring_attn_local)
  *   workspace >= ring_attn_bwd_local_workspace_bytes(...): two staging slots of K and V for the
  *             local devices, and delta / lse2
- * Blocks of steps s >= 1 are copied from their source shard into a staging slot on copy_stream,
- * double-buffered against the kernels on compute_stream (step 0 reads the shards in place); each
- * block's dk, dv accumulators are addressed where the block came from rather than copied along
- * (same arithmetic, no traffic).  Both streams are left ordered after all of the call's work.
+ * The blocks of steps s >= 1 arrive in a staging slot double-buffered against the kernels on
+ * compute_stream (step 0 reads the shards in place).  With bf16 inputs and D = 128 (not zigzag), a
+ * device that computes at step s hands its block to its local successor inside the step-s query-
+ * gradient kernel, as the forward does (the rows it stages in LDS are stored into the successor's
+ * slot; the host checks that every row of the block is staged); every other block is copied from its
+ * source shard on copy_stream.  Each block's dk, dv accumulators are addressed where the block came
+ * from rather than copied along (same arithmetic, no traffic).  RING_ATTN_HOP_STRESS (see
+ * ring_attn_local) applies here too.  Both streams are left ordered after all of the call's work.
  */
 int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_src, const void* o_local,
                         const void* dout_local, const float* lse_local, float* dq_local, float* dk, float* dv, int P,
