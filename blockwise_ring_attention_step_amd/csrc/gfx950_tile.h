@@ -51,10 +51,14 @@ __device__ __forceinline__ void wait_vmem() {
 // outstanding global load before such reads).  The kernels track completion themselves: vmcnt waits
 // and a workgroup barrier separate every copy from the first read of its stage.
 // The LDS address goes in M0 (bound through the operand constraint, so the compiler knows the
-// register's value); one wait state separates the M0 write from the load.
+// register's value).  The compiler cannot see the hazards of an instruction inside inline assembly,
+// so the block opens with the longest wait the load's operands need: 5 wait states, for a base
+// address whose SGPRs a VALU instruction has just written (v_readlane of a spilled SGPR, or
+// v_readfirstlane); a load issued sooner reads the stale register, and the wrong high address bits
+// fault.  It also covers the one wait state after the M0 write.
 __device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, uint32_t lds) {
   asm volatile(
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
       "s"(gbase), "{m0}"(lds)
       : "memory");
@@ -63,7 +67,7 @@ __device__ __forceinline__ void copy_to_lds16(const char* gbase, uint32_t voff, 
 // The same with 4 bytes per lane: lane l's dword at gbase + voff lands at LDS address lds + 4 l.
 __device__ __forceinline__ void copy_to_lds4(const char* gbase, uint32_t voff, uint32_t lds) {
   asm volatile(
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dword %0, %1" ::"v"(voff),
       "s"(gbase), "{m0}"(lds)
       : "memory");
