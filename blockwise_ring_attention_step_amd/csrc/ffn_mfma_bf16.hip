@@ -13,15 +13,16 @@
 // 4 waves and two workgroups per CU.  The waves form a (W/2) x 2 grid over the tile, each wave owning
 // (BM / (W/2)) x (BN/2) outputs as 32 x 32 accumulators (128 registers with 8 waves, so the 256 x 256
 // kernel holds everything in registers without spilling), held transposed (the lane is the token m,
-// the register the feature n, so that 4 consecutive features leave as one 8-byte store).  k advances in steps of
-// BK: the a and w rows of a step go HBM -> LDS directly (global_load_lds) into a ring of S buffers.
-// The steps of all of a workgroup's tiles form one stream: step s+S is requested into the buffer
-// of step s as soon as every wave has read it (one workgroup barrier per step), so S-1 steps are in
-// flight while one is multiplied, across tile boundaries too (the next tile's first steps load
-// while the current tile's epilogue runs).  Within a step, the LDS fragments of k slice kk+1 are
-// read while the products of slice kk run.  Tiles are numbered so that each XCD (workgroup id
-// mod 8) sweeps a contiguous range of them, GM m-tiles at a time, so the rows that neighbouring
-// workgroups share stay in that XCD's L2.
+// the register the feature n).  k advances in steps of BK: the a and w rows of a step go HBM -> LDS
+// directly (global_load_lds) into a ring of S buffers.  The steps of all of a workgroup's tiles form
+// one stream: step s+S is requested into the buffer of step s as soon as every wave has read it (one
+// workgroup barrier per step), so S-1 steps are in flight while one is multiplied, across tile
+// boundaries too (the next tile's first steps load while the current tile's epilogue runs).  Within a
+// step, the LDS fragments of k slice kk+1 are read while the products of slice kk run.  The epilogue
+// takes the bias from LDS (copied there during the tile's last steps) and sends each 32 x 32 output
+// block through a small LDS area of its wave, so that every store writes 64 contiguous bytes of a
+// row.  Tiles are numbered so that each XCD (workgroup id mod 8) sweeps a contiguous range of them,
+// GM m-tiles at a time, so the rows that neighbouring workgroups share stay in that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -83,7 +84,13 @@ __global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams
   static_assert(R == 64 || R == 128, "step rows of 64 or 128 bytes");
   static_assert(kPieces * kFfnWaves * RPP == BM + BN, "tile rows split evenly over the waves");
   static_assert((S - 1) * kPieces < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[S * kStage];
+  // after the S step buffers, 256 bytes per wave for the bias of its columns of the current tile
+  constexpr int kBiasOff = S * kStage;
+  static_assert(BN / WN <= 128, "one 256-byte bias copy per wave");
+  // then, per wave, a 32 x 32 block of the output on its way to HBM (rows padded from 64 to 80 bytes)
+  constexpr int kOutRow = 80;
+  constexpr int kOutOff = kBiasOff + 256 * W;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * kStage + 256 * W + 32 * kOutRow * W];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   // LDS layout of a step tile: 16-byte chunk c of row r is stored at chunk c ^ swz(r), so that the 16
@@ -167,61 +174,83 @@ __global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams
   const int a_row0 = wm * (BM / WM), w_row0 = kTileA / R + wn * (BN / WN);
 
   f32x16 acc[NB][MB];
-  // one set of fragments: products run bn-major (product i = NB-block i / MB, MB-block i % MB), so
-  // w fragment bn of the next k slice is read right after product MB bn + MB - 1, its last use in the
-  // current slice, and x fragment bm after product (NB - 1) MB + bm; each read lands in the register
-  // its predecessor just freed, at least MB products before its first use
-  bf16x8 wf[NB], xf[MB];
+  // Products run bn-major (product i = NB-block i / MB, MB-block i % MB).  The w fragment bn of the next k
+  // slice is read right after product MB bn + MB - 1, its last use in the current slice, into the register
+  // it frees, at least (NB - 1) MB products before its first use.  Every product of a slice reads all MB
+  // x fragments, so they are held twice, by slice parity: the next slice's x fragment bm is read after
+  // product bm of the current one, kProducts - 1 products before its first use (one set only would leave
+  // a single product between the read and the use, too short for LDS latency).
+  static_assert(KK % 2 == 0, "slice parity is the same in every step");
+  bf16x8 wf[NB], xf[2][MB];
   // fragment r of k slice kk (r < NB: w rows of block r; else x rows of block r - NB)
   auto read_one = [&](int buf, int kk, int r) {
     const LDS_AS char* base = smem + buf * kStage + roff[kk];
     if (r < NB)
       wf[r] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (w_row0 + 32 * r) * R));
     else
-      xf[r - NB] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (a_row0 + 32 * (r - NB)) * R));
+      xf[kk & 1][r - NB] = __builtin_bit_cast(bf16x8, *(const LDS_AS i16x8*)(base + (a_row0 + 32 * (r - NB)) * R));
   };
-  auto mfma_one = [&](int i) {
+  auto mfma_one = [&](int i, int kk) {
     const int bn = i / MB, bm = i % MB;
-    acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[bn], xf[bm], acc[bn][bm], 0, 0, 0);
+    acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[bn], xf[kk & 1][bm], acc[bn][bm], 0, 0, 0);
   };
-  // the fragment reads that follow product i: those whose last use in the slice is product i
+  // the fragment reads of slice kk that follow product i of the slice before it
   auto reads_after = [&](int i, int buf, int kk) {
-    if (i % MB == MB - 1) read_one(buf, kk, i / MB);            // w fragment bn = i / MB
-    if (i / MB == NB - 1) read_one(buf, kk, NB + i % MB);       // x fragment bm = i % MB
+    if (i % MB == MB - 1) read_one(buf, kk, i / MB);  // w fragment bn = i / MB (its last use was product i)
+    if (i < MB) read_one(buf, kk, NB + i);            // x fragment bm = i, into the other parity's set
   };
+
+  // The bias of the wave's BN / WN columns of the tile at n0 goes HBM -> LDS (4 bytes per lane, columns past
+  // the end re-read the last pair), requested at the start of step KT - S + 1 of the tile: the barrier wait of
+  // the tile's last step leaves only the (S - 2) kPieces most recent loads in flight, and the copies of the
+  // S - 2 steps between are that many loads younger than the bias copy.  (A tile of fewer steps requests it
+  // at its first step and waits for it before the epilogue.)  The epilogue then reads it from LDS: a global
+  // load there would wait for every store before it and for the next tile's copies.
+  auto request_bias = [&](int n0) {
+    const int c = min(n0 + wn * (BN / WN) + 2 * lane, p.N - 2);
+    copy_to_lds4((const char*)p.bias, (uint32_t)c * 2, (uint32_t)(uintptr_t)(smem + kBiasOff + wave * 256));
+  };
+  const LDS_AS char* bias_lds = smem + kBiasOff + wave * 256 + 8 * h2;
 
   // epilogue of the tile at (m0, n0): register 4 g + e of block (bn, bm) is feature
   // n = n0 + wn BN/WN + 32 bn + 8 g + 4 h2 + e of token m = m0 + wm BM/WM + 32 bm + j
-  const unsigned short* bias = (const unsigned short*)p.bias;
   unsigned short* out = (unsigned short*)p.out;
   // A tile that lies inside [0, M) x [0, N) stores without per-element bounds checks; only the edge
   // tiles take the checked form (its branches would otherwise keep accumulator values live across
   // every store and push the 256 x 256 kernel into scratch).
+  // Each 32 x 32 block passes through the wave's LDS staging area: lane (j, h2) writes its 16 values into
+  // row j, then every lane reads 16 bytes of one row (four lanes a row, 16 rows a pass) and stores them, so
+  // that each store writes 64 contiguous bytes of 16 output rows instead of 16 bytes of 32 rows.  The area
+  // belongs to one wave, whose LDS accesses execute in order, so no barrier is needed.
+  LDS_AS char* stage_out = smem + kOutOff + wave * (32 * kOutRow);
   auto epilogue_body = [&](int m0, int n0, auto checked_tag) {
     constexpr bool kChecked = decltype(checked_tag)::value;
 #pragma unroll
     for (int bn = 0; bn < NB; ++bn) {
-      const int nb = n0 + wn * (BN / WN) + 32 * bn + 4 * h2;
+      const int nblk = n0 + wn * (BN / WN) + 32 * bn;  // first feature of the block (N % 32 == 0)
       u16x4 bv[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nb + 8 * g;
-        bv[g] = (!kChecked || n < p.N) ? *(const u16x4*)(bias + n) : u16x4{0, 0, 0, 0};
-      }
+      for (int g = 0; g < 4; ++g)
+        bv[g] = (!kChecked || nblk < p.N) ? *(const LDS_AS u16x4*)(bias_lds + (32 * bn + 8 * g) * 2) : u16x4{0, 0, 0, 0};
 #pragma unroll
       for (int bm = 0; bm < MB; ++bm) {
-        const int m = m0 + wm * (BM / WM) + 32 * bm + j;
-        unsigned short* orow = out + (int64_t)m * p.ldo;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = nb + 8 * g;
           u16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = acc[bn][bm][4 * g + e] + __uint_as_float((uint32_t)bv[g][e] << 16);
             o[e] = __builtin_bit_cast(unsigned short, (__bf16)activate<ACT>(z));
           }
-          if (!kChecked || (m < p.M && n < p.N)) *(u16x4*)(orow + n) = o;
+          *(LDS_AS u16x4*)(stage_out + j * kOutRow + 16 * g + 8 * h2) = o;
+        }
+        const int mblk = m0 + wm * (BM / WM) + 32 * bm;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          const int r = 16 * pass + lane / 4, c = lane % 4;
+          const i16x8 v = *(const LDS_AS i16x8*)(stage_out + r * kOutRow + 16 * c);
+          if (!kChecked || (mblk + r < p.M && nblk < p.N))
+            *(i16x8*)(out + (int64_t)(mblk + r) * p.ldo + nblk + 8 * c) = v;
         }
       }
     }
@@ -234,25 +263,34 @@ __global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams
   };
 
   // One step: KK slices of NB x MB products.  After each product come the fragment reads it frees
-  // (reads_after) and, in the last slice, the step's other work in fixed slots (sched_barrier keeps
-  // the order): product 0 first meets the other waves at the barrier (step s+1 landed, step s read by
-  // all: the next step's fragments are read from buffer (s+1) % S only after it), and the copies of
-  // step s+S into the freed buffer follow products 1 .. kProducts-1, so that the matrix cores keep
-  // running across the barrier and the copies.  Near the end of the stream the same schedule runs on:
-  // requests past the last step fetch the last tile's rows again into buffers that no step reads, and
-  // the fragments read for a step past the last one are not used.
+  // (reads_after) and the step's other work in fixed slots (sched_barrier keeps the order).  In the last
+  // slice, product 0 first meets the other waves at the barrier (step s+1 landed, step s read by all:
+  // the next step's fragments are read from buffer (s+1) % S only after it), and the first half of the
+  // copies of step s+S into the freed buffer follows products 1 .. kProducts-1; the second half follows
+  // the products of the first slice of step s+1, so that fewer copies queue at the memory pipeline at
+  // once and the matrix cores keep running across the barrier and the copies.  (The barrier of step s+1
+  // waits for both halves.)  Near the end of the stream the same schedule runs on: requests past the
+  // last step fetch the last tile's rows again into buffers that no step reads, and the fragments read
+  // for a step past the last one are not used.
   constexpr int kProducts = NB * MB;
-  static_assert(kProducts >= 4, "slots for the barrier and copies");
+  static_assert(kProducts >= 4 && KK >= 2, "slots for the barrier and copies");
+  static_assert(S == 2 && kPieces % 2 == 0, "a request split over two steps fills the buffer the second frees");
   auto step = [&](int s) {
     const int buf = s % S;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < kProducts; ++i) {
-        mfma_one(i);
+        mfma_one(i, kk);
         __builtin_amdgcn_sched_barrier(0);
         if (kk + 1 < KK) {
           reads_after(i, buf, kk + 1);
+          if (kk == 0 && s > 0) {  // the second half of the request begun in step s-1 (the prologue's is whole)
+#pragma unroll
+            for (int k = kPieces / 2; k < kPieces; ++k)
+              if (1 + (k - kPieces / 2) * (kProducts - 1) / (kPieces / 2) == i) issue_piece(k, (s + 1) % S);
+            if (i == kProducts - 1) advance_request();
+          }
         } else {
           if (i == 0) {
             wait_vmem<(S - 2) * kPieces>();  // step s+1 has landed (this wave's copies)
@@ -260,13 +298,12 @@ __global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams
           }
           reads_after(i, (s + 1) % S, 0);
 #pragma unroll
-          for (int k = 0; k < kPieces; ++k)
-            if (1 + k * (kProducts - 1) / kPieces == i) issue_piece(k, buf);
+          for (int k = 0; k < kPieces / 2; ++k)
+            if (1 + k * (kProducts - 1) / (kPieces / 2) == i) issue_piece(k, buf);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    advance_request();
   };
 
   if (NS == 0) return;
@@ -285,9 +322,14 @@ __global__ __launch_bounds__(64 * W, OCC) void ffn_gemm_bf16(const FfnGemmParams
     for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
       for (int bm = 0; bm < MB; ++bm) acc[bn][bm] = f32x16{};
-    for (int kt = 0; kt < KT; ++kt) step(ti * KT + kt);
     int m0, n0;
     tile_of(ti, m0, n0);
+    const int kt_bias = max(KT - S + 1, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt == kt_bias) request_bias(n0);
+      step(ti * KT + kt);
+    }
+    if (KT - S + 1 < 0) wait_vmem<0>();
     epilogue(m0, n0);
   }
   wait_vmem<0>();  // no copy into LDS outlives the workgroup
