@@ -354,23 +354,28 @@ struct Fwd {
 };
 
 // Forward virtual tile v (stage ST): each lane stores back exactly the 16 bytes it copied into LDS, to
-// the same offset in the destination block; rows past the end of a ragged tile are not stored.
+// the same offset in the destination block (the lane's copy offset within a tile, cx.goff, from the
+// tile's first row there); rows past the end of a ragged tile are not stored.
 template <int ST>
 __device__ __forceinline__ void forward_tile(const Ctx& cx, const Fwd& fw, const LDS_AS char* smem, int v,
                                              int wave) {
   const int lane = __lane_id();
   const int key0 = (v - fw.v0) * kBc;
   const int64_t tofs = (int64_t)key0 * cx.row_bytes;
+  char* const kb = fw.kdst + tofs;
+  char* const vb = fw.vdst + tofs;
+  const bool full = key0 + kBc <= fw.nk;
 #pragma unroll
   for (int i = 0; i < kPiecesPerWave; ++i) {
-    const int row = (wave * kPiecesPerWave + i) * 4 + (lane >> 4);
     const LDS_AS char* src = smem + ST * kTileBytes + (wave * kPiecesPerWave + i) * 1024 + 16 * lane;
     const i16x8 kd = *(const LDS_AS i16x8*)src;
     const i16x8 vd = *(const LDS_AS i16x8*)(src + kVRing);
-    if (key0 + row < fw.nk) {
-      const int64_t off = tofs + (int64_t)row * cx.row_bytes + ((lane & 15) ^ swz(row)) * 16;
-      *(i16x8*)(fw.kdst + off) = kd;
-      *(i16x8*)(fw.vdst + off) = vd;
+    if (full) {
+      *(i16x8*)(kb + cx.goff[i]) = kd;
+      *(i16x8*)(vb + cx.goff[i]) = vd;
+    } else if (key0 + (wave * kPiecesPerWave + i) * 4 + (lane >> 4) < fw.nk) {
+      *(i16x8*)(kb + cx.goff[i]) = kd;
+      *(i16x8*)(vb + cx.goff[i]) = vd;
     }
   }
 }
