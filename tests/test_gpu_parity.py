@@ -380,11 +380,13 @@ def test_state_snapshot_and_resume(gpu_lib):
     assert max_err(unshard_lse(res[0][1], "contiguous"), ref_lse) <= TOL_BF16_LSE
 
 
-@pytest.mark.parametrize("D,dtype", [(5, "f32"), (5, "bf16"), (128, "bf16"), (128, "f32"), (12, "bf16")])
+@pytest.mark.parametrize("D,dtype", [(5, "f32"), (5, "bf16"), (128, "bf16"), (128, "f32"), (12, "bf16"), (64, "bf16"),
+                                     (48, "f32")])
 def test_finalize_divides_and_writes_lse(gpu_lib, D, dtype):
-    """ring_attn_finalize on a random valid state (the vector kernel for D % 4 == 0, the scalar one
-    otherwise): o = o_acc / l in token-major order, lse = (m + log2 l) ln 2, and o = 0, lse = -inf
-    where l = 0; checked against the same formulas in float64."""
+    """ring_attn_finalize on a random valid state (the four-load kernel for D % 16 == 0, with 8, 4 or 3
+    threads per row here; the one-load kernel for other D % 4 == 0; the scalar one otherwise):
+    o = o_acc / l in token-major order, lse = (m + log2 l) ln 2, and o = 0, lse = -inf where l = 0;
+    checked against the same formulas in float64."""
     ra = gpu_lib
     n_dev, B, Hq, Nq = 3, 2, 5, 37
     rng = np.random.default_rng(1800 + D)
