@@ -575,13 +575,35 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   float lsum = (sm.lpart[0] + sm.lpart[1]) + (sm.lpart[2] + sm.lpart[3]);
   const float M = sm.M;
 
-  // ---- epilogue: merge with the incoming state (or finalize)
+  // ---- epilogue: merge with the incoming state (or finalize).  The wave's 32 rows of o_acc are one
+  // contiguous 16 KiB run; they pass through LDS (the rings are free once every wave has left the loop):
+  // copied in whole rows, read by each lane in its accumulator layout, merged, written back, and stored
+  // in whole rows, so every global access of the state moves full 512-byte rows instead of 32 scattered
+  // 32-byte pieces.  The wave's area: row r (0..31) at wave * 16 KiB + r * 512, its 16-byte chunk c at
+  // position c ^ (r & 15), which spreads the 32 rows of one lane access over all banks.
   lsum += partner(lsum);
-  if (!qvalid) return;
-  const size_t srow = ((size_t)(dev * p.B + bb) * Hq + h) * NqT + row0 + qr;
-  float Mo = -INFINITY, lo = 0.f;
+  __syncthreads();  // every wave has left the loop: no LDS read of the rings is outstanding
+  const int wrow0 = qrow0 + wave * 32;                       // the wave's first row
+  const int nvalid = max(0, min(32, Nq - wrow0));            // its rows that exist
+  if (nvalid == 0) return;
+  const size_t srow0 = ((size_t)(dev * p.B + bb) * Hq + h) * NqT + row0 + wrow0;
+  const size_t srow = srow0 + j;
+  LDS_AS char* wl = smem + wave * (32 * kD * 4);
   const bool has_old = !(dfl & kDevInit);
+  float* const oacc_wave = p.o_acc + srow0 * kD;
+  // lane l of whole-row access k: row 2 k + l / 32, LDS position l % 32, global chunk (l % 32) ^ (row & 15)
+  const int xr = lane >> 5, xp = lane & 31;
   if (has_old) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + xr;
+      const int rs = min(r, nvalid - 1);  // rows past the end re-read the last row (not used)
+      copy_to_lds16((const char*)oacc_wave, (uint32_t)(rs * kD * 4 + ((xp ^ (r & 15)) * 16)),
+                    (uint32_t)(uintptr_t)(wl + k * 1024));
+    }
+  }
+  float Mo = -INFINITY, lo = 0.f;
+  if (has_old && qvalid) {
     Mo = p.m[srow];
     lo = p.l[srow];
   }
@@ -589,18 +611,24 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   const float ao = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - Mf);
   const float an = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
   const float lf = ao * lo + an * lsum;
-  float* oacc_row = p.o_acc + srow * kD;
-  // the incoming accumulator rows, all requested before any store (one memory round trip, not one
-  // per chunk); this lane's chunk c covers d = 32 (c / 4) + 8 (c % 4) + 4 h2 .. + 3
+  // this lane's chunk (dt, gq): d = 32 dt + 8 gq + 4 h2 .. + 3, global chunk 8 dt + 2 gq + h2 of row j
+  auto lane_chunk = [&](int c) -> LDS_AS char* {
+    return wl + j * (kD * 4) + ((((8 * (c >> 2) + 2 * (c & 3) + h2)) ^ (j & 15)) * 16);
+  };
   f32x4 old[16];
+  if (has_old) {
+    wait_vmem<0>();  // this wave's copies have landed (the area is the wave's own: no barrier)
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-    old[c] = has_old ? *(const f32x4*)(oacc_row + 32 * (c >> 2) + 8 * (c & 3) + 4 * h2) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 16; ++c) old[c] = *(const LDS_AS f32x4*)lane_chunk(c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) old[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (dfl & kDevFinal) {
+    // O rows in bf16 (256 bytes each; a wave's rows are Hq * D * 2 bytes apart): staged as 32 rows of
+    // 256 bytes, chunk c at position c ^ (row & 15), then stored four whole rows per instruction
     const float inv = lf > 0.f ? 1.0f / lf : 0.f;
-    unsigned short* orow =
-        (unsigned short*)p.o_out + (((size_t)dev * p.B + bb) * NqT + row0 + qr) * (size_t)Hq * kD + (size_t)h * kD;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const int dt = c >> 2, gq = c & 3;
@@ -610,9 +638,19 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
         const float val = (ao * old[c][i] + an * o[dt][4 * gq + i]) * inv;
         outv[i] = __builtin_bit_cast(unsigned short, (__bf16)val);
       }
-      *(u16x4*)(orow + 32 * dt + 8 * gq + 4 * h2) = outv;
+      // 8-byte piece (dt, gq, h2) of the row: 16-byte chunk 4 dt + gq, half h2
+      *(LDS_AS u16x4*)(wl + j * (kD * 2) + (((4 * dt + gq) ^ (j & 15)) * 16) + 8 * h2) = outv;
     }
-    if (h2 == 0 && p.lse_out) p.lse_out[srow] = lf > 0.f ? (Mf + log2f(lf)) * kLn2 : -INFINITY;
+    unsigned short* const orow0 =
+        (unsigned short*)p.o_out + (((size_t)dev * p.B + bb) * NqT + row0 + wrow0) * (size_t)Hq * kD + (size_t)h * kD;
+    const int yr = lane >> 4, yp = lane & 15;  // four rows per instruction, 16 chunks of 16 bytes each
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + yr;
+      const i16x8 v8 = *(const LDS_AS i16x8*)(wl + r * (kD * 2) + yp * 16);
+      if (r < nvalid) *(i16x8*)(orow0 + (size_t)r * Hq * kD + 8 * (yp ^ (r & 15))) = v8;
+    }
+    if (h2 == 0 && qvalid && p.lse_out) p.lse_out[srow] = lf > 0.f ? (Mf + log2f(lf)) * kLn2 : -INFINITY;
   } else {
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -620,9 +658,15 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
       f32x4 nv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) nv[i] = ao * old[c][i] + an * o[dt][4 * gq + i];
-      *(f32x4*)(oacc_row + 32 * dt + 8 * gq + 4 * h2) = nv;
+      *(LDS_AS f32x4*)lane_chunk(c) = nv;
     }
-    if (h2 == 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + xr;
+      const f32x4 v4 = *(const LDS_AS f32x4*)(wl + r * (kD * 4) + xp * 16);
+      if (r < nvalid) *(f32x4*)(oacc_wave + r * kD + 4 * (xp ^ (r & 15))) = v4;
+    }
+    if (h2 == 0 && qvalid) {
       p.m[srow] = Mf;
       p.l[srow] = lf;
     }
