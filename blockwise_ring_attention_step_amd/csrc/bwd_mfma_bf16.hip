@@ -26,6 +26,7 @@
 // chunk (bwd_dkv).  Tiles go HBM -> LDS directly (global_load_lds) through 3-stage rings in the
 // swizzled layout of gfx950_tile.h; tile t+2 is requested while tile t is computed and one
 // workgroup barrier per tile makes the next one visible.
+#include <algorithm>
 #include <type_traits>
 
 #include "gfx950_tile.h"
@@ -57,6 +58,49 @@ __device__ __forceinline__ void load_tile_pieces(const TileSrc& src, uint32_t ld
     const int srow = row < src.nrows ? row : src.nrows - 1;
     const uint32_t off = (uint32_t)(srow * src.row_bytes) + (((lane & 15) ^ swz(row)) * 16);
     copy_to_lds16(src.base, off, lds_tile + piece * 1024);
+  }
+}
+
+// The epilogue of both kernels: dst[row] = (init ? 0 : dst[row]) + mul * acc for the wave's 32 rows of a
+// token-major fp32 array (row r of the wave at base + r * stride floats, kD floats each; rows >= nvalid are
+// not touched), where lane (j, h2) holds row j, d = 32 dt + 8 g + 4 h2 + i in acc[dt][4 g + i].  The rows
+// pass through the wave's 16 KiB LDS area wl (row r at r * 512, its 16-byte chunk c at position
+// c ^ (r & 15), which spreads the 32 rows of one lane access over all banks): copied in whole rows,
+// accumulated in the lanes' layout, and stored in whole rows, so that every global access moves whole
+// 512-byte rows instead of 32 scattered 32-byte pieces.  The area must be free of other use (the caller
+// passes a workgroup barrier after its last LDS read of the tiles).
+__device__ __forceinline__ void accumulate_rows(float* base, int64_t stride, int nvalid, bool init, float mul,
+                                                const f32x16 (&acc)[4], LDS_AS char* wl) {
+  // the lane index, computed here rather than kept in a register across the caller's tile loop
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int j = lane & 31, h2 = lane >> 5;
+  const int xr = lane >> 5, xp = lane & 31;  // whole-row access k: row 2 k + xr, LDS position xp
+  if (!init) {
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + xr;
+      const int rs = min(r, nvalid - 1);  // rows past the end re-read the last row (not stored)
+      copy_to_lds16((const char*)base, (uint32_t)(rs * stride * 4 + ((xp ^ (r & 15)) * 16)),
+                    (uint32_t)(uintptr_t)(wl + k * 1024));
+    }
+    wait_vmem<0>();  // this wave's copies have landed (the area is the wave's own)
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int dt = c >> 2, g = c & 3;
+    LDS_AS f32x4* slot = (LDS_AS f32x4*)(wl + j * (kD * 4) + (((8 * dt + 2 * g + h2) ^ (j & 15)) * 16));
+    const f32x4 old = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *slot;
+    f32x4 nv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nv[i] = old[i] + mul * acc[dt][4 * g + i];
+    *slot = nv;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = 2 * k + xr;
+    const f32x4 v4 = *(const LDS_AS f32x4*)(wl + r * (kD * 4) + xp * 16);
+    if (r < nvalid) *(f32x4*)(base + r * stride + 4 * (xp ^ (r & 15))) = v4;
   }
 }
 
@@ -197,7 +241,8 @@ __device__ __forceinline__ void dq_request(const DqCtx& cx, int t, int stage, co
 }
 
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kDqVRing];
+  // the K and V rings; the epilogue reuses 16 KiB per wave
+  __shared__ __attribute__((aligned(1024))) char smem_raw[std::max(2 * kDqVRing, kDqWaves * 32 * kD * 4)];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -363,22 +408,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
     tile(std::integral_constant<int, 2>{}, t + 2);
   }
 
-  // epilogue: dq (token-major, fp32) += scale * dQ; lane's row, d = 32 dt + 8 g + 4 h2 + i
-  if (!qvalid) return;
-  float* dqrow = p.dq + (((size_t)qdev * p.B + bb) * p.NqTot + row0 + qr) * qrow_elems + (size_t)h * kD;
-  const bool init = p.flags[dl] & kBwdInitDq;
-  f32x4 old[16];
-#pragma unroll
-  for (int cI = 0; cI < 16; ++cI)
-    old[cI] = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(dqrow + 32 * (cI >> 2) + 8 * (cI & 3) + 4 * h2);
-#pragma unroll
-  for (int cI = 0; cI < 16; ++cI) {
-    const int dt = cI >> 2, g = cI & 3;
-    f32x4 nv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nv[i] = old[cI][i] + p.scale * dqt[dt][4 * g + i];
-    *(f32x4*)(dqrow + 32 * dt + 8 * g + 4 * h2) = nv;
-  }
+  // epilogue: dq (token-major, fp32) += scale * dQ for the wave's 32 rows (every wave has left the loop)
+  __syncthreads();
+  const int erow0 = qt * kDqRows + wave * 32;  // the wave's first row
+  const int nvalid = max(0, min(32, Nq - erow0));
+  if (nvalid == 0) return;
+  float* const dq0 = p.dq + (((size_t)qdev * p.B + bb) * p.NqTot + row0 + erow0) * qrow_elems + (size_t)h * kD;
+  accumulate_rows(dq0, (int64_t)qrow_elems, nvalid, p.flags[dl] & kBwdInitDq, p.scale, dqt, smem + wave * (32 * kD * 4));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -426,7 +462,8 @@ __device__ __forceinline__ void kv_request(const KvCtx& cx, int stage, int hq, i
 }
 
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kBwdStages * kKvStageBytes + kKvPBytes];
+  // the Q / dO ring and the P buffers; the epilogue reuses 16 KiB per wave
+  __shared__ __attribute__((aligned(1024))) char smem_raw[std::max(kBwdStages * kKvStageBytes + kKvPBytes, kKvWaves * 32 * kD * 4)];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -631,24 +668,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
     tile(std::integral_constant<int, 2>{}, it + 2);
   }
 
-  // epilogue: dk += scale * dK or dv += dV (token-major, fp32); lane's key, d = 32 dt + 8 g + 4 h2 + i
-  if (!kvalid) return;
-  const size_t grow = (((size_t)gdev * p.B + bb) * p.NkTot + key) * krow_elems + (size_t)kvh * kD;
-  float* row = (key_wave ? p.dk : p.dv) + grow;
-  const float mul = key_wave ? p.scale : 1.f;
-  const bool init = p.flags[dl] & kBwdInitDkv;
-  f32x4 old[16];
-#pragma unroll
-  for (int cI = 0; cI < 16; ++cI)
-    old[cI] = init ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)(row + 32 * (cI >> 2) + 8 * (cI & 3) + 4 * h2);
-#pragma unroll
-  for (int cI = 0; cI < 16; ++cI) {
-    const int dt = cI >> 2, g = cI & 3;
-    f32x4 nv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nv[i] = old[cI][i] + mul * acc[dt][4 * g + i];
-    *(f32x4*)(row + 32 * dt + 8 * g + 4 * h2) = nv;
-  }
+  // epilogue: dk += scale * dK (key wave) or dv += dV (value wave) for the wave's 32 keys (every wave has
+  // left the loop)
+  __syncthreads();
+  const int wkey0 = ktile * kKvKeys + (wave & 3) * 32;
+  const int nvalid = max(0, min(32, nk - wkey0));
+  if (nvalid == 0) return;
+  float* const row0p = (key_wave ? p.dk : p.dv) + (((size_t)gdev * p.B + bb) * p.NkTot + wkey0) * krow_elems + (size_t)kvh * kD;
+  accumulate_rows(row0p, (int64_t)krow_elems, nvalid, p.flags[dl] & kBwdInitDkv, key_wave ? p.scale : 1.f, acc,
+                  smem + wave * (32 * kD * 4));
 }
 
 // ------------------------------------------------------------------------------------------------
