@@ -56,6 +56,9 @@ constexpr int kBc = 64;                       // keys per tile
 constexpr int kTileBytes = kBc * kRowBytes;   // 16 KiB
 constexpr int kStages = 4;
 constexpr int kVRing = kStages * kTileBytes;  // LDS: K ring [0, 64 KiB), V ring [64 KiB, 128 KiB)
+constexpr int kQStageBytes = 32 * kRowBytes;  // a wave's 32 query rows, staged in the prologue
+static_assert(2 * kVRing + 4 * kQStageBytes <= 160 * 1024, "LDS of gfx950");
+static_assert(4 * kQStageBytes <= 2 * kTileBytes, "waves 4-7 stage their rows in K stages 2 and 3");
 constexpr int kPrefetch = 2;                  // tiles requested ahead of the one being computed
 constexpr int kPiecesPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB load instructions per tile per wave
 
@@ -409,7 +412,8 @@ __device__ __forceinline__ void tile_windows(const Ctx& cx, const Frags& f, cons
 }
 
 __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kVRing];
+  // the K and V rings, then 32 KiB that (with K stages 2 and 3) stage the query rows in the prologue
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kVRing + 4 * kQStageBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -452,16 +456,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   lp.h2 = h2;
   lp.c = p.scale_log2;
 
-  // ---- Q^T fragments: lane holds q[row qr][16*kk + 8*h2 .. +7]
+  // ---- Q^T fragments (read in the prologue): lane holds q[row qr][16*kk + 8*h2 .. +7]
   Frags f;
-  const size_t q_dev = (size_t)p.B * NqT * Hq * kD;
-  const unsigned short* qrow = (const unsigned short*)p.q + dev * q_dev +
-                               ((size_t)bb * NqT + row0 + (qvalid ? qr : 0)) * Hq * kD + h * kD + 8 * h2;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    i16x8 raw = qvalid ? *(const i16x8*)(qrow + 16 * kk) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    f.q[kk] = __builtin_bit_cast(bf16x8, raw);
-  }
 
   // ---- the blocks this slot folds: rows of this (batch, kv head), and the key ranges: the workgroup
   // loads tiles up to its last row's limit; each group computes up to its own last row's limit; masks
@@ -537,7 +533,26 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
   Softmax sm;
 
   if (cx.total > 0) {
-    // prologue: the first kPrefetch tiles
+    // prologue: the wave's 32 query rows (a row of 256 bytes every Hq * D * 2 bytes) go to LDS in whole
+    // rows, row r at qs + r * 256 with its 16-byte chunk c at position c ^ (r & 15), while the first
+    // kPrefetch tiles are requested; each lane then reads its fragments from there.  (Waves 0-3 stage in
+    // the 32 KiB after the rings, waves 4-7 in K stages 2 and 3, which no request reaches before the
+    // barrier below.)
+    const int wrow0 = qrow0 + wave * 32;
+    const int nqv = max(0, min(32, Nq - wrow0));  // the wave's rows that exist
+    const LDS_AS char* qs =
+        smem + (wave < kWaves / 2 ? 2 * kVRing + wave * kQStageBytes : 2 * kTileBytes + (wave - kWaves / 2) * kQStageBytes);
+    if (nqv > 0) {
+      const char* q0 = (const char*)p.q +
+                       2 * ((size_t)dev * p.B * NqT * Hq * kD + (((size_t)bb * NqT + row0 + wrow0) * Hq + h) * kD);
+      const int qr_l = lane >> 4, qp = lane & 15;  // copy k: row 4 k + qr_l, LDS position qp
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + qr_l;
+        const int rs = min(r, nqv - 1);  // rows past the end re-read the last row (zeroed below)
+        copy_to_lds16(q0, (uint32_t)(rs * Hq * kD * 2 + ((qp ^ (r & 15)) * 16)), (uint32_t)(uintptr_t)(qs + k * 1024));
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kPrefetch; ++t)
       if (t < cx.total) {
@@ -551,6 +566,12 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_bf16_d128(const StepPar
       z[tid + kThreads] = i16x8{};
     }
     wait_vmem_all();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const i16x8 raw = qvalid ? *(const LDS_AS i16x8*)(qs + j * kRowBytes + (((2 * kk + h2) ^ (j & 15)) * 16))
+                               : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      f.q[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
     __syncthreads();
     f32x16 s[2];
     bf16x8 pf[4];
