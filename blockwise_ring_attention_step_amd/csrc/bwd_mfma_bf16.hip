@@ -198,6 +198,9 @@ constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kDqVRing = kBwdStages * kTileBytes;  // LDS: K ring, then V ring
 constexpr int kDqPieces = 16 / kDqWaves;           // 1 KiB pieces per wave per K (and per V) tile
+constexpr int kDqStageRows = 32 * kRowBytes;       // a wave's 32 rows of Q (or dO), staged in the prologue
+static_assert(kBwdStages == 3 && 4 * kDqStageRows <= 2 * kTileBytes, "waves 0-3 (4-7) stage Q in K (V) stages 1-2");
+static_assert(2 * kDqVRing + 8 * kDqStageRows <= 160 * 1024, "dO of every wave above the rings");
 
 struct DqCtx {
   TileSrc k, v;            // tile 0 of this pair's keys and values
@@ -242,7 +245,7 @@ __device__ __forceinline__ void dq_request(const DqCtx& cx, int t, int stage, co
 
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParams p) {
   // the K and V rings; the epilogue reuses 16 KiB per wave
-  __shared__ __attribute__((aligned(1024))) char smem_raw[std::max(2 * kDqVRing, kDqWaves * 32 * kD * 4)];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[std::max(2 * kDqVRing + kDqWaves * kDqStageRows, kDqWaves * 32 * kD * 4)];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -284,14 +287,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 
   // this lane's row: Q^T and dO^T fragments (B operands), lse2 and delta
   const size_t qrow_elems = (size_t)p.Hq * kD;
-  const size_t qbase = (((size_t)qdev * p.B + bb) * p.NqTot + row0 + (qvalid ? qr : 0)) * qrow_elems + (size_t)h * kD;
-  bf16x8 qf[8], df[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const i16x8 zq = {0, 0, 0, 0, 0, 0, 0, 0};
-    qf[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const i16x8*)((const unsigned short*)p.q + qbase + 16 * kk + 8 * h2) : zq);
-    df[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const i16x8*)((const unsigned short*)p.dout + qbase + 16 * kk + 8 * h2) : zq);
-  }
+  bf16x8 qf[8], df[8];  // read in the prologue below
   const size_t srow = (((size_t)qdev * p.B + bb) * p.Hq + h) * p.NqTot + row0 + (qvalid ? qr : 0);
   const float lse2 = qvalid ? p.lse2[srow] : INFINITY;  // +inf for a row that saw no key: p = 0
   const float delta = qvalid ? p.delta[srow] : 0.f;
@@ -324,11 +320,40 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dqt[dt] = f32x16{};
 
-  if (ntiles > 0)
-    for (int t = 0; t < 2 && t < ntiles; ++t) dq_request(cx, t, t, smem);
-  // on every path into the loop (see bwd_dkv): the Q^T / dO^T fragment loads are complete
-  wait_vmem<0>();
-  __syncthreads();
+  // Prologue: the wave's 32 query rows of Q and dO (256 bytes each, Hq * D * 2 bytes apart) go to LDS in
+  // whole rows, row r at r * 256 of the wave's area with its 16-byte chunk c at position c ^ (r & 15),
+  // beside the request of key tile 0; each lane reads its fragments from there.  The areas are the parts
+  // of the rings that tile 0 does not use (stages 1 and 2 of K and V) and the LDS above them; tile 1 is
+  // requested once every wave has read its fragments.
+  {
+    const int srow0 = qt * kDqRows + wave * 32;
+    const int nqv = max(0, min(32, Nq - srow0));  // the wave's rows that exist
+    const LDS_AS char* qst = smem + (wave < 4 ? kTileBytes + wave * kDqStageRows : kDqVRing + kTileBytes + (wave - 4) * kDqStageRows);
+    const LDS_AS char* dst = smem + 2 * kDqVRing + wave * kDqStageRows;
+    if (nqv > 0) {
+      const size_t q0 = 2 * ((((size_t)qdev * p.B + bb) * p.NqTot + row0 + srow0) * qrow_elems + (size_t)h * kD);
+      const int r_l = lane >> 4, cp = lane & 15;  // copy k: row 4 k + r_l, LDS position cp
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + r_l;
+        const uint32_t off = (uint32_t)(min(r, nqv - 1) * qrow_elems * 2 + ((cp ^ (r & 15)) * 16));
+        copy_to_lds16((const char*)p.q + q0, off, (uint32_t)(uintptr_t)(qst + k * 1024));
+        copy_to_lds16((const char*)p.dout + q0, off, (uint32_t)(uintptr_t)(dst + k * 1024));
+      }
+    }
+    if (ntiles > 0) dq_request(cx, 0, 0, smem);
+    // on every path into the loop (see bwd_dkv): every load so far is complete
+    wait_vmem<0>();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int pos = ((2 * kk + h2) ^ (j & 15)) * 16;
+      const i16x8 zq = {0, 0, 0, 0, 0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const LDS_AS i16x8*)(qst + j * kRowBytes + pos) : zq);
+      df[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const LDS_AS i16x8*)(dst + j * kRowBytes + pos) : zq);
+    }
+    __syncthreads();  // every wave has its fragments: the areas may now take tile 1
+    if (ntiles > 1) dq_request(cx, 1, 1, smem);
+  }
   // one key tile (t, LDS stage ST = t % 3); unrolled by three below so that every LDS address is a
   // per-lane base plus an immediate
   auto tile = [&](auto stage_tag, int t) {
