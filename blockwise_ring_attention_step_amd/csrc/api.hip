@@ -1259,7 +1259,151 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
     RA_CHECK(ra::launch_zero_f32(dk, dkv_bytes / 4, cs));
     RA_CHECK(ra::launch_zero_f32(dv, dkv_bytes / 4, cs));
   }
-  for (int s = 0; s < P; ++s) {
+  // the fields every launch shares
+  ra::BwdParams base{};
+  base.q = q_local;
+  base.dout = dout_local;
+  base.lse2 = lse2;
+  base.delta = delta;
+  base.dq = dq_local;
+  base.dk = dk;
+  base.dv = dv;
+  base.B = B;
+  base.Hq = Hq;
+  base.Hkv = Hkv;
+  base.Nq = n / nh;
+  base.NqTot = n;
+  base.NkTot = n;
+  base.D = D;
+  base.causal = causal ? 1 : 0;
+  base.scale = scale;
+  base.scale_log2 = (float)(scale * kLog2e);
+
+  // Whole ring local (dev0 = 0) with the bf16 D=128 kernels: two ring steps per query-gradient launch,
+  // as in the forward.  Pair L covers steps s0 = 2L and s1 = 2L + 1.  Device i's block of s0 is in its
+  // part of slot L & 1 (its own shard at L = 0); its block of s1 is what its predecessor holds at s0,
+  // in device i - 1's part of the same slot (shard i - 1 at L = 0).  One bwd_dq launch folds both
+  // blocks into each device's query gradient, writing it once, and hands the s1 block on to device
+  // i + 1's part of slot (L + 1) & 1 where its workgroups stage all of it (push); the two bwd_dkv
+  // launches (s0, then s1: device i's s1 block is device i - 1's s0 block, so their key/value gradient
+  // rows coincide) read the same two blocks.  Blocks not pushed arrive by copy from their source shard.
+  // Slot L & 1 is only read and slot (L + 1) & 1 only written during pair L.
+  const bool two_step = in_step_hop && n_local == P && P >= 2 && steps_per_launch() == 2;
+  if (two_step) {
+    const int NL = (P + 1) / 2;
+    const int64_t st = layout_stride(layout, P);
+    auto blockj = [&](int i, int s) { return ((i - s) % P + P) % P; };
+    std::vector<uint8_t> push((size_t)NL * P, 0);
+    for (int L = 0; L + 1 < NL; ++L)
+      for (int i = 0; i < P; ++i) {
+        const int s1 = 2 * L + 1;
+        if (cls[(size_t)s1 * n_units + i] == 0) continue;
+        if (step_forward_covers(causal, block_offset(layout, P, n, i), st, n,
+                                block_offset(layout, P, n, blockj(i, s1)), st, n))
+          push[(size_t)L * P + i] = 1;
+      }
+    auto pair_needs_copy = [&](int L) -> bool {  // pair L's slot L & 1 has a block not pushed by pair L-1
+      if (L <= 0 || L >= NL) return false;
+      for (int x = 0; x < P; ++x)
+        if (!push[(size_t)(L - 1) * P + (x + P - 1) % P]) return true;
+      return false;
+    };
+    auto pair_copies = [&](int L) -> hipError_t {  // device x's block of step 2L, from its source shard
+      const int sl = L & 1;
+      for (int x = 0; x < P;) {
+        if (push[(size_t)(L - 1) * P + (x + P - 1) % P]) {
+          ++x;
+          continue;
+        }
+        const int j0 = blockj(x, 2 * L);
+        int x2 = x + 1;
+        while (x2 < P && !push[(size_t)(L - 1) * P + x2 - 1] && blockj(x2, 2 * L) == j0 + (x2 - x)) ++x2;
+        const size_t bytes = (size_t)(x2 - x) * blk;
+        hipError_t e = poison(hs, stage_k[sl] + x * blk, bytes, xs);
+        if (e == hipSuccess) e = poison(hs, stage_v[sl] + x * blk, bytes, xs);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(stage_k[sl] + x * blk, ksrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(stage_v[sl] + x * blk, vsrc + (size_t)j0 * blk, bytes, hipMemcpyDeviceToDevice, xs);
+        if (e != hipSuccess) return e;
+        x = x2;
+      }
+      return hipSuccess;
+    };
+    for (int L = 0; L < NL; ++L) {
+      const int s0 = 2 * L, s1 = 2 * L + 1;
+      if (pair_needs_copy(L + 1)) {  // copies for pair L+1, into the slot that pair L-1 read
+        if (L >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(L + 1) & 1], 0));
+        RA_CHECK(jitter(hs.jitter_copy, xs));
+        RA_CHECK(pair_copies(L + 1));
+        RA_CHECK(hipEventRecord(ev_copy[(L + 1) & 1], xs));
+      }
+      if (pair_needs_copy(L)) RA_CHECK(hipStreamWaitEvent(cs, ev_copy[L & 1], 0));
+      ra::BwdParams p = base;
+      p.k = L == 0 ? (const void*)ksrc : (const void*)stage_k[L & 1];
+      p.v = L == 0 ? (const void*)vsrc : (const void*)stage_v[L & 1];
+      p.fwd_k = stage_k[(L + 1) & 1];
+      p.fwd_v = stage_v[(L + 1) & 1];
+      // query gradients of both steps
+      p.n_launch = 0;
+      for (int i = 0; i < P; ++i) {
+        const bool c0 = cls[(size_t)s0 * n_units + i] != 0, c1 = s1 < P && cls[(size_t)s1 * n_units + i] != 0;
+        if (!c0 && !c1) continue;
+        const int x = p.n_launch++;
+        const Unit u0 = ring_unit(causal, layout, P, n, i, blockj(i, s0), 0);
+        p.qslot[x] = i;
+        p.kvslot[x] = i;
+        p.kvslot2[x] = (i + P - 1) % P;
+        p.gslot[x] = blockj(i, s0);
+        p.q_row0[x] = u0.row0;
+        p.q_off[x] = u0.q_off;
+        p.q_stride = p.k_stride = u0.stride;
+        p.nk[x] = c0 ? u0.nk : 0;
+        p.k_off[x] = u0.k_off;
+        if (c1) {
+          const Unit u1 = ring_unit(causal, layout, P, n, i, blockj(i, s1), 0);
+          p.nk2[x] = u1.nk;
+          p.k_off2[x] = u1.k_off;
+        }
+        p.Nk = std::max({p.Nk, p.nk[x], p.nk2[x]});
+        p.flags[x] = dq_first[i] == s0 || dq_first[i] == s1 ? ra::kBwdInitDq : 0;
+        const bool pushes = push[(size_t)L * P + i] != 0;
+        p.fwd[x] = pushes ? (i + 1) % P : -1;
+        if (pushes) {  // slot (L+1) & 1 was last read by pair L-1, earlier on this stream
+          RA_CHECK(poison(hs, stage_k[(L + 1) & 1] + (size_t)((i + 1) % P) * blk, blk, cs));
+          RA_CHECK(poison(hs, stage_v[(L + 1) & 1] + (size_t)((i + 1) % P) * blk, blk, cs));
+        }
+      }
+      RA_CHECK(jitter(hs.jitter_compute, cs));
+      if (p.n_launch > 0) RA_CHECK(launch_bwd(p, dtype, true, cs));
+      // key/value gradients, one launch per step
+      for (int s = s0; s <= s1 && s < P; ++s) {
+        ra::BwdParams pk = base;
+        pk.k = p.k;
+        pk.v = p.v;
+        pk.n_launch = 0;
+        for (int i = 0; i < P; ++i) {
+          if (cls[(size_t)s * n_units + i] == 0) continue;
+          const int x = pk.n_launch++;
+          const Unit un = ring_unit(causal, layout, P, n, i, blockj(i, s), 0);
+          pk.qslot[x] = i;
+          pk.kvslot[x] = s == s0 ? i : (i + P - 1) % P;
+          pk.gslot[x] = blockj(i, s);
+          pk.q_row0[x] = un.row0;
+          pk.q_off[x] = un.q_off;
+          pk.q_stride = pk.k_stride = un.stride;
+          pk.nk[x] = un.nk;
+          pk.k_off[x] = un.k_off;
+          pk.Nk = std::max(pk.Nk, un.nk);
+          pk.flags[x] = first_flags[(size_t)s * n_units + i] & ra::kBwdInitDkv;
+          pk.fwd[x] = -1;
+        }
+        if (pk.n_launch > 0) RA_CHECK(launch_bwd(pk, dtype, false, cs));
+      }
+      if (pair_needs_copy(L + 2)) RA_CHECK(hipEventRecord(ev_comp[L & 1], cs));
+    }
+  }
+  for (int s = 0; s < P && !two_step; ++s) {
     if (needs_copy(s + 1)) {  // copies for step s+1, into the slot that step s-1 read
       if (s >= 1) RA_CHECK(hipStreamWaitEvent(xs, ev_comp[(s + 1) & 1], 0));
       RA_CHECK(jitter(hs.jitter_copy, xs));

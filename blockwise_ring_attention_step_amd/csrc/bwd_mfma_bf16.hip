@@ -204,8 +204,10 @@ static_assert(2 * kDqVRing + 8 * kDqStageRows <= 160 * 1024, "dO of every wave a
 
 struct DqCtx {
   TileSrc k, v;            // tile 0 of this pair's keys and values
+  TileSrc k2, v2;          // tile 0 of the second block's (two ring steps in one launch)
   int64_t tile_stride;     // bytes from one key tile to the next
-  int nk;
+  int nk, nk2;             // keys of the first and second block (nk2 = 0: none)
+  int nt0;                 // tiles of the first block in the stream (the second block's follow)
   int wave;
 };
 
@@ -213,7 +215,7 @@ struct DqCtx {
 // back to the same offsets of the destination block (the successor's receive slot).  Each lane stores the
 // 16 bytes it copied itself, so its own vmcnt wait for the copy is all the ordering needed; rows past the
 // end of a ragged block are not stored.
-__device__ __forceinline__ void dq_forward(const DqCtx& cx, char* kdst, char* vdst, int t, int stage,
+__device__ __forceinline__ void dq_forward(const DqCtx& cx, char* kdst, char* vdst, int t, int nk, int stage,
                                            const LDS_AS char* smem) {
   const int lane = __lane_id();
   const int key0 = t * kTile;
@@ -225,7 +227,7 @@ __device__ __forceinline__ void dq_forward(const DqCtx& cx, char* kdst, char* vd
     const LDS_AS char* src = smem + stage * kTileBytes + piece * 1024 + 16 * lane;
     const i16x8 kd = *(const LDS_AS i16x8*)src;
     const i16x8 vd = *(const LDS_AS i16x8*)(src + kDqVRing);
-    if (key0 + row < cx.nk) {
+    if (key0 + row < nk) {
       const int64_t off = tofs + (int64_t)row * cx.k.row_bytes + ((lane & 15) ^ swz(row)) * 16;
       *(i16x8*)(kdst + off) = kd;
       *(i16x8*)(vdst + off) = vd;
@@ -234,10 +236,12 @@ __device__ __forceinline__ void dq_forward(const DqCtx& cx, char* kdst, char* vd
 }
 
 __device__ __forceinline__ void dq_request(const DqCtx& cx, int t, int stage, const LDS_AS char* smem) {
-  TileSrc k = cx.k, v = cx.v;
-  k.base += t * cx.tile_stride;
-  v.base += t * cx.tile_stride;
-  k.nrows = v.nrows = min(kTile, cx.nk - t * kTile);
+  const bool second = t >= cx.nt0;  // stream tile t is tile t - nt0 of the second block
+  TileSrc k = second ? cx.k2 : cx.k, v = second ? cx.v2 : cx.v;
+  const int tt = second ? t - cx.nt0 : t;
+  k.base += tt * cx.tile_stride;
+  v.base += tt * cx.tile_stride;
+  k.nrows = v.nrows = min(kTile, (second ? cx.nk2 : cx.nk) - tt * kTile);
   const uint32_t kl = (uint32_t)(uintptr_t)(smem + stage * kTileBytes);
   load_tile_pieces(k, kl, cx.wave * kDqPieces, kDqPieces);
   load_tile_pieces(v, kl + kDqVRing, cx.wave * kDqPieces, kDqPieces);
@@ -265,25 +269,31 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   const int dl = bt / p.B, bb = bt - dl * p.B;
   const int h = kvh * gsz + hq;
   const int qt = p.causal ? p.n_qtiles - 1 - qt_rank : qt_rank;
-  const int qdev = p.qslot[dl], kvdev = p.kvslot[dl];
-  const int Nq = p.Nq, nk = p.nk[dl], row0 = p.q_row0[dl];
+  const int qdev = p.qslot[dl], kvdev = p.kvslot[dl], kvdev2 = p.kvslot2[dl];
+  const int Nq = p.Nq, nk = p.nk[dl], nk2 = p.nk2[dl], row0 = p.q_row0[dl];
   const int qr = qt * kDqRows + wave * 32 + j;  // this lane's query row within the slot
   const bool qvalid = qr < Nq;
   const int qlast = min(qt * kDqRows + kDqRows, Nq) - 1;
 
-  // causal range: last visible key of this lane's row, of the wave's rows and of the workgroup's
-  auto last_key = [&](int row) -> int {
-    if (!p.causal) return nk - 1;
-    const int64_t d = p.q_off[dl] + (int64_t)row * p.q_stride - p.k_off[dl];
+  // causal range, per block (the first, and the second of a two-step launch): last visible key of this
+  // lane's row, of the wave's rows and of the workgroup's
+  auto last_key = [&](int row, int64_t k_off, int n_k) -> int {
+    if (n_k <= 0) return -1;
+    if (!p.causal) return n_k - 1;
+    const int64_t d = p.q_off[dl] + (int64_t)row * p.q_stride - k_off;
     if (d < 0) return -1;
     const int64_t kk = d / p.k_stride;
-    return kk < (int64_t)(nk - 1) ? (int)kk : nk - 1;
+    return kk < (int64_t)(n_k - 1) ? (int)kk : n_k - 1;
   };
-  const int kmax_lane = last_key(qvalid ? qr : qlast);
   const int wrow0 = min(qt * kDqRows + wave * 32, qlast), wrow1 = min(qt * kDqRows + wave * 32 + 31, qlast);
-  const int kmin_wave = last_key(wrow0), kmax_wave = last_key(wrow1);
-  const int kend = last_key(qlast);
-  const int ntiles = kend < 0 ? 0 : kend / kTile + 1;
+  const int64_t koff0 = p.k_off[dl], koff1 = p.k_off2[dl];
+  const int kmax_lane0 = last_key(qvalid ? qr : qlast, koff0, nk);
+  const int kmax_lane1 = last_key(qvalid ? qr : qlast, koff1, nk2);
+  const int kmin_wave0 = last_key(wrow0, koff0, nk), kmax_wave0 = last_key(wrow1, koff0, nk);
+  const int kmin_wave1 = last_key(wrow0, koff1, nk2), kmax_wave1 = last_key(wrow1, koff1, nk2);
+  const int kend0 = last_key(qlast, koff0, nk), kend1 = last_key(qlast, koff1, nk2);
+  const int ntiles0 = kend0 < 0 ? 0 : kend0 / kTile + 1;
+  const int ntiles = ntiles0 + (kend1 < 0 ? 0 : kend1 / kTile + 1);
 
   // this lane's row: Q^T and dO^T fragments (B operands), lse2 and delta
   const size_t qrow_elems = (size_t)p.Hq * kD;
@@ -298,21 +308,28 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   const size_t kv_off = 2 * ((((size_t)kvdev * p.B + bb) * p.NkTot) * p.Hkv * kD + (size_t)kvh * kD);
   cx.k = TileSrc{(const char*)p.k + kv_off, krow_bytes, kTile};
   cx.v = TileSrc{(const char*)p.v + kv_off, krow_bytes, kTile};
+  const size_t kv_off2 = 2 * ((((size_t)kvdev2 * p.B + bb) * p.NkTot) * p.Hkv * kD + (size_t)kvh * kD);
+  cx.k2 = TileSrc{(const char*)p.k + kv_off2, krow_bytes, kTile};
+  cx.v2 = TileSrc{(const char*)p.v + kv_off2, krow_bytes, kTile};
   cx.tile_stride = kTile * krow_bytes;
   cx.nk = nk;
+  cx.nk2 = nk2;
+  cx.nt0 = ntiles0;
   cx.wave = wave;
   const TileOffsets to = tile_offsets();
   // the hop inside the step: the workgroups of the first query head of each key/value head hand the
-  // block on to the successor's receive slot, each the 256 keys that line up with its query tile
-  // (tiles [fw_lo, fw_hi) of the block, all of which it loads)
+  // block on to the successor's receive slot (the second block, in a two-step launch), each the 256 keys
+  // that line up with its query tile (tiles [fw_lo, fw_hi) of the stream, all of which it loads)
   char* fw_k = nullptr;
   char* fw_v = nullptr;
-  int fw_lo = 0, fw_hi = 0;
+  int fw_lo = 0, fw_hi = 0, fw_t0 = 0, fw_nk = 0;
   if (p.fwd[dl] >= 0 && hq == 0 && p.fwd_k && p.fwd_v) {
     const size_t fw_off = 2 * ((((size_t)p.fwd[dl] * p.B + bb) * p.NkTot) * p.Hkv * kD + (size_t)kvh * kD);
     fw_k = (char*)p.fwd_k + fw_off;
     fw_v = (char*)p.fwd_v + fw_off;
-    fw_lo = qt * (kDqRows / kTile);
+    fw_t0 = nk2 > 0 ? ntiles0 : 0;  // the handed-on block's first stream tile
+    fw_nk = nk2 > 0 ? nk2 : nk;
+    fw_lo = fw_t0 + qt * (kDqRows / kTile);
     fw_hi = min(fw_lo + kDqRows / kTile, ntiles);
   }
 
@@ -359,7 +376,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
   auto tile = [&](auto stage_tag, int t) {
     constexpr int ST = decltype(stage_tag)::value;
     const LDS_AS char* kt = smem + ST * kTileBytes;
-    const int key0 = t * kTile;
+    const bool second = t >= ntiles0;  // a tile of the second block
+    const int key0 = (second ? t - ntiles0 : t) * kTile;  // within its block
+    const int kmax_wave = second ? kmax_wave1 : kmax_wave0, kmin_wave = second ? kmin_wave1 : kmin_wave0;
     const bool work = key0 <= kmax_wave;  // else no row of this wave sees the tile
     const bool masked = key0 + kTile - 1 > kmin_wave;
     // per 32-key half cc: 16 products S^T / dP^T (even / odd items, k step item / 2; A = K / V rows),
@@ -382,7 +401,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
     if (work) stream_preload<16, kAheadBwd>(rsd, op_sd(C0{}));
     // the hop's stores go out before this tile's request, so that the wait at the tile's end (all but
     // the latest request) also covers them and the vmcnt counts stay those of the copies
-    if (t >= fw_lo && t < fw_hi) dq_forward(cx, fw_k, fw_v, t, ST, smem);
+    if (t >= fw_lo && t < fw_hi) dq_forward(cx, fw_k, fw_v, t - fw_t0, fw_nk, ST, smem);
     if (t + 2 < ntiles) dq_request(cx, t + 2, (ST + 2) % kBwdStages, smem);
     auto half = [&](auto ccc) {
       constexpr int CC = decltype(ccc)::value;
@@ -402,7 +421,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_bf16_d128(const BwdParam
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * CC + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (key > kmax_lane) pr[r] = 0.f;
+          if (key > (second ? kmax_lane1 : kmax_lane0)) pr[r] = 0.f;
         }
       }
 #pragma unroll

@@ -48,6 +48,11 @@ struct BwdParams {
   int64_t k_off[RA_MAX_DEV];
   uint8_t flags[RA_MAX_DEV];
   int fwd[RA_MAX_DEV];  // bwd_dq: device position in fwd_k / fwd_v that slot t's block is handed to, or -1
+  // bwd_dq only: a second key/value block folded after the first in the same launch (two ring steps;
+  // nk2[t] = 0: none).  With a second block, fwd[t] hands on the second block.
+  int kvslot2[RA_MAX_DEV];
+  int nk2[RA_MAX_DEV];
+  int64_t k_off2[RA_MAX_DEV];
 };
 
 // One projection of the blockwise feed-forward: out[m, n] = act(sum_k x[m, k] w[n, k] + bias[n]) in

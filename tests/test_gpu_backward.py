@@ -122,6 +122,19 @@ def test_bwd_ring_small(gpu_lib, causal, layout, n):
     _check(2, 4, n, 4, 2, causal, layout, 900 + n)
 
 
+@pytest.mark.parametrize("steps_per_launch", ["1", "2"])
+@pytest.mark.parametrize("P,n,causal,layout", [(3, 200, True, "contiguous"), (5, 96, True, "striped"),
+                                               (4, 160, False, "contiguous"), (2, 320, True, "striped"),
+                                               (5, 72, True, "contiguous")])
+def test_bwd_ring_one_and_two_steps_per_launch(gpu_lib, monkeypatch, steps_per_launch, P, n, causal, layout):
+    """With the whole ring local, each query-gradient launch folds two ring steps (the block the device
+    holds and its predecessor's, the latter handed on to the successor's next slot from inside the
+    kernel); RING_ATTN_STEPS_PER_LAUNCH=1 keeps one step per launch.  Odd P ends on a one-step launch;
+    contiguous causal rings pair a visible block with a fully masked one; both paths against the oracle."""
+    monkeypatch.setenv("RING_ATTN_STEPS_PER_LAUNCH", steps_per_launch)
+    _check(1, P, n, 4, 2, causal, layout, 1700 + 10 * P + n)
+
+
 @pytest.mark.parametrize("causal,n", [(True, 128), (True, 200), (False, 96)])
 def test_bwd_zigzag_ring(gpu_lib, causal, n):
     """Zigzag shards: each device's two chunks are separate units (ragged chunks of 64, 100, 48 rows)."""

@@ -83,9 +83,11 @@ def test_forward_ring_unchanged_under_hop_stress(gpu_lib, monkeypatch, case):
     monkeypatch.delenv("RING_ATTN_HOP_STRESS", raising=False)
 
 
+@pytest.mark.parametrize("steps_per_launch", ["1", "2"])
 @pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
-def test_backward_ring_unchanged_under_hop_stress(gpu_lib, monkeypatch, layout):
+def test_backward_ring_unchanged_under_hop_stress(gpu_lib, monkeypatch, layout, steps_per_launch):
     ra = gpu_lib
+    monkeypatch.setenv("RING_ATTN_STEPS_PER_LAUNCH", steps_per_launch)
     P, n, Hq, Hkv, D = 4, 256, 4, 2, 128
     S = P * n
     q, k, v = _inputs(S, Hq, Hkv, D, 1400, "bf16")
