@@ -1284,10 +1284,11 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
   // part of slot L & 1 (its own shard at L = 0); its block of s1 is what its predecessor holds at s0,
   // in device i - 1's part of the same slot (shard i - 1 at L = 0).  One bwd_dq launch folds both
   // blocks into each device's query gradient, writing it once, and hands the s1 block on to device
-  // i + 1's part of slot (L + 1) & 1 where its workgroups stage all of it (push); the two bwd_dkv
-  // launches (s0, then s1: device i's s1 block is device i - 1's s0 block, so their key/value gradient
-  // rows coincide) read the same two blocks.  Blocks not pushed arrive by copy from their source shard.
-  // Slot L & 1 is only read and slot (L + 1) & 1 only written during pair L.
+  // i + 1's part of slot (L + 1) & 1 where its workgroups stage all of it (push); one bwd_dkv launch
+  // folds, into each block's key/value gradient, the queries of the device that holds it at s0 and of
+  // that device's successor (which sees the block at s1), writing it once.  Blocks not pushed arrive
+  // by copy from their source shard.  Slot L & 1 is only read and slot (L + 1) & 1 only written during
+  // pair L.
   const bool two_step = in_step_hop && n_local == P && P >= 2 && steps_per_launch() == 2;
   if (two_step) {
     const int NL = (P + 1) / 2;
@@ -1376,30 +1377,38 @@ int ring_attn_bwd_local(const void* q_local, const void* k_src, const void* v_sr
       }
       RA_CHECK(jitter(hs.jitter_compute, cs));
       if (p.n_launch > 0) RA_CHECK(launch_bwd(p, dtype, true, cs));
-      // key/value gradients, one launch per step
-      for (int s = s0; s <= s1 && s < P; ++s) {
-        ra::BwdParams pk = base;
-        pk.k = p.k;
-        pk.v = p.v;
-        pk.n_launch = 0;
-        for (int i = 0; i < P; ++i) {
-          if (cls[(size_t)s * n_units + i] == 0) continue;
-          const int x = pk.n_launch++;
-          const Unit un = ring_unit(causal, layout, P, n, i, blockj(i, s), 0);
-          pk.qslot[x] = i;
-          pk.kvslot[x] = s == s0 ? i : (i + P - 1) % P;
-          pk.gslot[x] = blockj(i, s);
-          pk.q_row0[x] = un.row0;
-          pk.q_off[x] = un.q_off;
-          pk.q_stride = pk.k_stride = un.stride;
-          pk.nk[x] = un.nk;
-          pk.k_off[x] = un.k_off;
-          pk.Nk = std::max(pk.Nk, un.nk);
-          pk.flags[x] = first_flags[(size_t)s * n_units + i] & ra::kBwdInitDkv;
-          pk.fwd[x] = -1;
+      // key/value gradients of both steps in one launch: block j meets the queries of a = j + s0 (step
+      // s0, the device that holds it) and of b = j + s1 (step s1, which reads it from a's part of the
+      // slot), and its gradient rows are written once
+      ra::BwdParams pk = base;
+      pk.k = p.k;
+      pk.v = p.v;
+      pk.n_launch = 0;
+      for (int j = 0; j < P; ++j) {
+        const int a = (j + s0) % P, b = (j + s1) % P;
+        const bool ca = cls[(size_t)s0 * n_units + a] != 0, cb = s1 < P && cls[(size_t)s1 * n_units + b] != 0;
+        if (!ca && !cb) continue;
+        const int x = pk.n_launch++;
+        const Unit ua = ring_unit(causal, layout, P, n, a, j, 0), ub = ring_unit(causal, layout, P, n, b, j, 0);
+        const Unit& u0 = ca ? ua : ub;
+        pk.qslot[x] = ca ? a : b;
+        pk.kvslot[x] = a;
+        pk.gslot[x] = j;
+        pk.q_row0[x] = u0.row0;
+        pk.q_off[x] = u0.q_off;
+        pk.q_stride = pk.k_stride = u0.stride;
+        pk.nk[x] = u0.nk;
+        pk.k_off[x] = u0.k_off;
+        pk.Nk = std::max(pk.Nk, u0.nk);
+        if (ca && cb) {
+          pk.two_q[x] = 1;
+          pk.qslot2[x] = b;
+          pk.q_off2[x] = ub.q_off;
         }
-        if (pk.n_launch > 0) RA_CHECK(launch_bwd(pk, dtype, false, cs));
+        pk.flags[x] = dkv_first[j] == s0 || dkv_first[j] == s1 ? ra::kBwdInitDkv : 0;
+        pk.fwd[x] = -1;
       }
+      if (pk.n_launch > 0) RA_CHECK(launch_bwd(pk, dtype, false, cs));
       if (pair_needs_copy(L + 2)) RA_CHECK(hipEventRecord(ev_comp[L & 1], cs));
     }
   }

@@ -168,7 +168,7 @@ hipError_t launch_bwd_generic(const BwdParams& p, int dtype, bool dq_pass, hipSt
   if (z <= 0) return hipSuccess;
   if (z > 65535 || p.Hq > 65535) return hipErrorInvalidConfiguration;
   for (int x = 0; x < p.n_launch; ++x)
-    if (p.nk2[x] != 0) return hipErrorInvalidValue;  // one key/value block per launch slot here
+    if (p.nk2[x] != 0 || p.two_q[x]) return hipErrorInvalidValue;  // one block, one query device per slot here
   const int rows = dq_pass ? p.Nq : p.Nk;
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)(dq_pass ? p.Hq : p.Hkv),

@@ -484,21 +484,24 @@ struct KvCtx {
   const char* delta;
   int64_t row_bytes;    // Hq * D * 2
   int64_t head_stat;    // bytes from one query head's lse2 / delta rows to the next (NqTot * 4)
+  int64_t part_rows;    // bytes from the first query device's q / dout rows to the second's
+  int64_t part_stat;    // and from its lse2 / delta rows to the second's
   int nq;
   int wave;
 };
 
-// request tile (query head hq, query tile qt) into a stage: 2 Q + 2 dO pieces per wave, and 16 lanes
-// of 4 bytes of lse2 (waves 0-3: rows 16 w .. + 15) or delta (waves 4-7)
-__device__ __forceinline__ void kv_request(const KvCtx& cx, int stage, int hq, int qt, const LDS_AS char* smem) {
+// request tile (query device part, query head hq, query tile qt) into a stage: 2 Q + 2 dO pieces per
+// wave, and 16 lanes of 4 bytes of lse2 (waves 0-3: rows 16 w .. + 15) or delta (waves 4-7)
+__device__ __forceinline__ void kv_request(const KvCtx& cx, int stage, int part, int hq, int qt,
+                                           const LDS_AS char* smem) {
   const uint32_t st = (uint32_t)(uintptr_t)(smem + stage * kKvStageBytes);
   const int nrows = min(kTile, cx.nq - qt * kTile);
-  const int64_t rowsel = (int64_t)qt * kTile * cx.row_bytes + (int64_t)hq * kD * 2;
+  const int64_t rowsel = (int64_t)qt * kTile * cx.row_bytes + (int64_t)hq * kD * 2 + (part ? cx.part_rows : 0);
   load_tile_pieces(TileSrc{cx.q + rowsel, cx.row_bytes, nrows}, st, cx.wave * kKvPieces, kKvPieces);
   load_tile_pieces(TileSrc{cx.dout + rowsel, cx.row_bytes, nrows}, st + kTileBytes, cx.wave * kKvPieces, kKvPieces);
   const int lane = __lane_id();
   if (lane < 16) {
-    const char* src = (cx.wave < 4 ? cx.lse2 : cx.delta) + hq * cx.head_stat;
+    const char* src = (cx.wave < 4 ? cx.lse2 : cx.delta) + hq * cx.head_stat + (part ? cx.part_stat : 0);
     const int row = qt * kTile + (cx.wave & 3) * 16 + lane;
     const int srow = row < cx.nq ? row : cx.nq - 1;  // rows past the end re-read the last (masked)
     copy_to_lds4(src, (uint32_t)(srow * 4), st + 2 * kTileBytes + (cx.wave >> 2) * 256 + (cx.wave & 3) * 64);
@@ -527,26 +530,33 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   const int dl = bt / p.B, bb = bt - dl * p.B;
   const int gsz = p.Hq / p.Hkv;
   const int qdev = p.qslot[dl], kvdev = p.kvslot[dl], gdev = p.gslot[dl];
+  const bool two = p.two_q[dl] != 0;  // a second query device (part 1) after the first (part 0)
+  const int qdev2 = two ? p.qslot2[dl] : qdev;
   const int Nq = p.Nq, nk = p.nk[dl], row0 = p.q_row0[dl];
   if (ktile * kKvKeys >= nk) return;
   const int key = ktile * kKvKeys + (wave & 3) * 32 + j;  // this lane's key
   const bool kvalid = key < nk;
 
-  // causal: first query row that sees this lane's key, of the wave's keys and of the workgroup's
-  auto first_row = [&](int kk) -> int {
+  // causal, per part: first query row that sees this lane's key, of the wave's keys and of the workgroup's
+  auto first_row = [&](int kk, int64_t q_off) -> int {
     if (!p.causal) return 0;
-    const int64_t d = p.k_off[dl] + (int64_t)kk * p.k_stride - p.q_off[dl];
+    const int64_t d = p.k_off[dl] + (int64_t)kk * p.k_stride - q_off;
     if (d <= 0) return 0;
     const int64_t r = (d + p.q_stride - 1) / p.q_stride;
     return r < (int64_t)Nq ? (int)r : Nq;
   };
+  const int64_t qo0 = p.q_off[dl], qo1 = two ? p.q_off2[dl] : qo0;
   const int klast = min(ktile * kKvKeys + kKvKeys, nk) - 1;
-  const int qmin_lane = first_row(kvalid ? key : klast);
+  const int qmin_lane0 = first_row(kvalid ? key : klast, qo0), qmin_lane1 = first_row(kvalid ? key : klast, qo1);
   const int wk0 = min(ktile * kKvKeys + (wave & 3) * 32, klast), wk1 = min(ktile * kKvKeys + (wave & 3) * 32 + 31, klast);
-  const int qmin_wave = first_row(wk0), qmax_wave = first_row(wk1);  // rows >= qmax_wave see every key of the wave
-  const int qt_first = first_row(ktile * kKvKeys) / kTile;
+  // rows >= qmax_wave see every key of the wave
+  const int qmin_wave0 = first_row(wk0, qo0), qmax_wave0 = first_row(wk1, qo0);
+  const int qmin_wave1 = first_row(wk0, qo1), qmax_wave1 = first_row(wk1, qo1);
+  const int qt_first0 = first_row(ktile * kKvKeys, qo0) / kTile, qt_first1 = first_row(ktile * kKvKeys, qo1) / kTile;
   const int nqt = (Nq + kTile - 1) / kTile;
-  const int nitems = (nqt - qt_first) * gsz;  // (query head, query tile) pairs, head-major
+  // (query head, query tile) pairs, head-major, of part 0 and then of part 1
+  const int nitems0 = (nqt - qt_first0) * gsz;
+  const int nitems = nitems0 + (two ? (nqt - qt_first1) * gsz : 0);
 
   // this lane's key: K^T fragments (B operand of S, value wave) or V^T fragments (of dP, key wave)
   const size_t krow_elems = (size_t)p.Hkv * kD;
@@ -568,6 +578,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   cx.lse2 = (const char*)p.lse2 + stat0;
   cx.delta = (const char*)p.delta + stat0;
   cx.head_stat = (int64_t)p.NqTot * 4;
+  cx.part_rows = (int64_t)(qdev2 - qdev) * p.B * p.NqTot * cx.row_bytes;
+  cx.part_stat = (int64_t)(qdev2 - qdev) * p.B * p.Hq * cx.head_stat;
   cx.nq = Nq;
   cx.wave = wave;
   const TileOffsets to = tile_offsets();
@@ -577,19 +589,24 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  // items walk (query head, query tile) head-major: the query tile of the current item, and the
-  // item requested next
-  int qt = qt_first, rhq = 0, rqt = qt_first;
-  auto advance = [&](int& h_, int& q_) {
-    if (++q_ == nqt) {
-      q_ = qt_first;
-      ++h_;
+  // items walk part 0 and then part 1, each (query head, query tile) head-major: the query tile of the
+  // current item, and the item requested next
+  int qt = nitems0 > 0 ? qt_first0 : qt_first1;
+  int rpart = nitems0 > 0 ? 0 : 1, rhq = 0, rqt = qt;
+  auto advance = [&]() {
+    if (++rqt == nqt) {
+      rqt = rpart ? qt_first1 : qt_first0;
+      if (++rhq == gsz && rpart == 0) {
+        rpart = 1;
+        rhq = 0;
+        rqt = qt_first1;
+      }
     }
   };
   if (nitems > 0) {
     for (int it = 0; it < 2 && it < nitems; ++it) {
-      kv_request(cx, it, rhq, rqt, smem);
-      advance(rhq, rqt);
+      kv_request(cx, it, rpart, rhq, rqt, smem);
+      advance();
     }
   }
   // on every path into the loop, including the empty one: the compiler's wait bookkeeping then knows
@@ -607,7 +624,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
   auto tile = [&](auto stage_tag, int it) {
     constexpr int ST = decltype(stage_tag)::value;
     const int q0 = qt * kTile;
-    qt = qt + 1 == nqt ? qt_first : qt + 1;
+    const bool part1 = it >= nitems0;
+    qt = qt + 1 == nqt ? (it + 1 >= nitems0 ? qt_first1 : qt_first0) : qt + 1;
+    const int qmin_wave = part1 ? qmin_wave1 : qmin_wave0, qmax_wave = part1 ? qmax_wave1 : qmax_wave0;
     const bool work = q0 + kTile > qmin_wave;  // else no key of this wave (pair) is seen by the tile's rows
     const LDS_AS char* st = smem + ST * kKvStageBytes;
     const LDS_AS char* qtl = st;
@@ -624,8 +643,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
     OperandRing<kAheadBwd> ring;
     if (work) stream_preload<16, kAheadBwd>(ring, op1);
     if (it + 2 < nitems) {
-      kv_request(cx, (ST + 2) % kBwdStages, rhq, rqt, smem);
-      advance(rhq, rqt);
+      kv_request(cx, (ST + 2) % kBwdStages, rpart, rhq, rqt, smem);
+      advance();
     }
     f32x16 t2[2];
     bf16x8 pk[2][2];  // value wave: P in bf16, the B operands of dV^T += dO^T P
@@ -650,7 +669,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_bf16_d128(const BwdPara
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int row = q0 + 32 * c2 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-              if (row < qmin_lane || row >= Nq) x[r] = 0.f;
+              if (row < (part1 ? qmin_lane1 : qmin_lane0) || row >= Nq) x[r] = 0.f;
             }
           }
 #pragma unroll

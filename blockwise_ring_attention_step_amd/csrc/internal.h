@@ -53,6 +53,11 @@ struct BwdParams {
   int kvslot2[RA_MAX_DEV];
   int nk2[RA_MAX_DEV];
   int64_t k_off2[RA_MAX_DEV];
+  // bwd_dkv only: where two_q[t] != 0, the query rows of device qslot2[t] (the same q_row0, position
+  // q_off2[t]) also see slot t's block, folded after those of qslot[t] in the same launch
+  uint8_t two_q[RA_MAX_DEV];
+  int qslot2[RA_MAX_DEV];
+  int64_t q_off2[RA_MAX_DEV];
 };
 
 // One projection of the blockwise feed-forward: out[m, n] = act(sum_k x[m, k] w[n, k] + bias[n]) in
