@@ -190,6 +190,10 @@ int ring_attn_finalize(const float* o_acc, const float* m, const float* l, void*
  *                         then shows as NaN); "jitter-copy" / "jitter-compute" put a bounded sleep
  *                         kernel (about 0.2 ms) before each step's hop copies / each step kernel.
  *                         Results must not change.  ring_attn_bwd_local honours the same three.
+ *   RING_ATTN_STEPS_PER_LAUNCH=1  one ring step per kernel launch where the whole ring is local
+ *                         (n_local == P, device source, bf16, D = 128), instead of two: the second
+ *                         block of a launch is pulled from the predecessor's slot and pushed on to
+ *                         the successor's next slot.  The same switch applies to ring_attn_bwd_local.
  *   RING_ATTN_FAIL_AT_STEP=k  (0 <= k < P) enqueue steps [0, k) only, without the fused final
  *                         division, give every local device that has not computed yet the empty
  *                         state, join the streams and return RA_ERR_INJECTED.  The workspace state is
@@ -312,7 +316,9 @@ int ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* 
  * device that computes at step s hands its block to its local successor inside the step-s query-
  * gradient kernel, as the forward does (the rows it stages in LDS are stored into the successor's
  * slot; the host checks that every row of the block is staged); every other block is copied from its
- * source shard on copy_stream.  Each block's dk, dv accumulators are addressed where the block came
+ * source shard on copy_stream.  When, in addition, the whole ring is local (n_local == P), each pair of
+ * steps 2L, 2L + 1 runs as one query-gradient and one key/value-gradient launch, with the schedule of
+ * ring_attn_local's two-step launches (the gradients are the same up to fp32 summation order).  Each block's dk, dv accumulators are addressed where the block came
  * from rather than copied along (same arithmetic, no traffic).  RING_ATTN_HOP_STRESS (see
  * ring_attn_local) applies here too.  Both streams are left ordered after all of the call's work.
  */
