@@ -21,6 +21,10 @@
 //            that reads its key/value head, and computes, per 32-row chunk,
 //              S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = K^T / V^T in VGPRs),
 //              dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose reads).
+// A launch may cover two ring steps (every device local): bwd_dq then streams the tiles of two key/value
+// blocks, the one the device holds and its predecessor's, as one sequence with per-block causal limits,
+// and bwd_dkv the query tiles of two devices, the block's holder and the holder's successor, each with
+// its own limits; either way every gradient row is written once per launch.
 // In both, the lane of an accumulator is its stationary row (query or key), so the per-row scalars
 // (lse2, delta) or per-column ones come as one value per lane (bwd_dq) or four 16-byte LDS reads per
 // chunk (bwd_dkv).  Tiles go HBM -> LDS directly (global_load_lds) through 3-stage rings in the
