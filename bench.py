@@ -19,6 +19,10 @@ fraction of the dense bf16 MFMA rate at that clock.
 FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T and P.V), so causal
 runs count only the visible pairs; the backward counts 10*D (five products of that size); the
 feed-forward 4 d_model d_ff per token (two products).  Printed on stdout: one JSON line.  Progress goes to stderr.
+
+Diagnostics (no benchmark line): ``--copy-calibration`` (a plain 1 GiB copy, the reference for HBM byte
+counters), ``--gemm-calibration`` (a library bf16 GEMM on N(0,1) and on constant operands with the GFX
+clock: the rate a dense MFMA load sustains on this machine), ``--inputs constant``.
 """
 from __future__ import annotations
 
@@ -452,6 +456,51 @@ def sample_clock_once(call, torch, ms_per_call, seconds):
         amdsmi.amdsmi_shut_down()
 
 
+def gemm_calibration(torch, measure_clock=True, n=8192, seconds=2.0):
+    """Sustained rate of a plain library GEMM (torch.mm of two contiguous n x n bf16 matrices, fp32
+    accumulation inside hipBLASLt) on seeded N(0,1) operands and on operands that are all 1.0, with the
+    GFX clock under each load: a reference for what a dense MFMA stream attains on this machine for the data
+    it runs on, beside the 2.5 PFLOP/s published peak (quoted at 2.4 GHz).  One JSON line per input."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    flops = 2.0 * n ** 3
+    for kind in ("normal", "constant"):
+        if kind == "normal":
+            a = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+            b = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+        else:
+            a = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
+            b = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+
+        def call():
+            torch.mm(a, b, out=c)
+
+        t0 = time.time()
+        while time.time() - t0 < 1.0:  # warm-up: the clock settles under the load
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        calls = max(20, int(seconds * 1e3 / (e0.elapsed_time(e1) / 20)))  # about `seconds` of timed calls
+        e0.record()
+        for _ in range(calls):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
+        tflops = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_calibration": kind, "n": n, "calls": calls, "ms_per_call": ms, "tflops": tflops,
+                          "pct_of_peak": 100 * tflops / PEAK_BF16_TFLOPS, "sclk_mhz": sclk, "sclk_gpu_busy": busy,
+                          "pct_of_peak_at_sclk": 100 * tflops / clock_peak(sclk) if sclk else None}), flush=True)
+        del a, b, c
+
+
 def traffic_entry():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it belongs to this kernel source."""
     try:
@@ -540,6 +589,9 @@ def main():
                          "the clock depends on operand bit activity (the kernels execute the same instructions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="only time a library bf16 GEMM (torch.mm, 8192^3) on seeded N(0,1) and on constant operands "
+                         "for about 2 s each, with the GFX clock: what a dense MFMA load sustains on this box")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -562,6 +614,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copied 3 x 1 GiB")
+        return
+    if args.gemm_calibration:
+        gemm_calibration(torch, not args.no_clock)
         return
     w = si.WORKLOADS[args.workload]
     main_res = run_workload(w, args.steps, args.warmup, not args.no_clock, args.inputs)
