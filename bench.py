@@ -20,6 +20,10 @@ FLOPs are algorithmic: 4*D per visible (query, key) pair per query head (Q.K^T a
 runs count only the visible pairs; the backward counts 10*D (five products of that size); the
 feed-forward 4 d_model d_ff per token (two products).  Printed on stdout: one JSON line.  Progress goes to stderr.
 
+The line also carries ``gemm_reference``: a library bf16 GEMM (torch.mm, 8192^3) timed on seeded N(0,1)
+operands after the workloads, with its clock, and ``roofline.frac_of_gemm_reference``, the step kernel's
+rate over that GEMM's (``--no-gemm-reference`` skips it).
+
 Diagnostics (no benchmark line): ``--copy-calibration`` (a plain 1 GiB copy, the reference for HBM byte
 counters), ``--gemm-calibration`` (a library bf16 GEMM on N(0,1) and on constant operands with the GFX
 clock: the rate a dense MFMA load sustains on this machine), ``--inputs constant``.
@@ -456,49 +460,47 @@ def sample_clock_once(call, torch, ms_per_call, seconds):
         amdsmi.amdsmi_shut_down()
 
 
-def gemm_calibration(torch, measure_clock=True, n=8192, seconds=2.0):
+def gemm_rate(torch, kind, measure_clock=True, n=8192, seconds=2.0):
     """Sustained rate of a plain library GEMM (torch.mm of two contiguous n x n bf16 matrices, fp32
-    accumulation inside hipBLASLt) on seeded N(0,1) operands and on operands that are all 1.0, with the
-    GFX clock under each load: a reference for what a dense MFMA stream attains on this machine for the data
-    it runs on, beside the 2.5 PFLOP/s published peak (quoted at 2.4 GHz).  One JSON line per input."""
+    accumulation inside hipBLASLt) on seeded N(0,1) operands (kind "normal") or on operands that are all
+    1.0 ("constant"), with the GFX clock under that load: a reference for what a dense MFMA stream
+    attains on this machine for the data it runs on, beside the 2.5 PFLOP/s published peak (quoted at
+    2.4 GHz)."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
-    flops = 2.0 * n ** 3
-    for kind in ("normal", "constant"):
-        if kind == "normal":
-            a = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
-            b = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
-        else:
-            a = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
-            b = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
-        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    if kind == "normal":
+        a = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+    else:
+        a = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.ones(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
 
-        def call():
-            torch.mm(a, b, out=c)
+    def call():
+        torch.mm(a, b, out=c)
 
-        t0 = time.time()
-        while time.time() - t0 < 1.0:  # warm-up: the clock settles under the load
-            call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        calls = max(20, int(seconds * 1e3 / (e0.elapsed_time(e1) / 20)))  # about `seconds` of timed calls
-        e0.record()
-        for _ in range(calls):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / calls
-        sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
-        tflops = flops / (ms * 1e-3) / 1e12
-        print(json.dumps({"gemm_calibration": kind, "n": n, "calls": calls, "ms_per_call": ms, "tflops": tflops,
-                          "pct_of_peak": 100 * tflops / PEAK_BF16_TFLOPS, "sclk_mhz": sclk, "sclk_gpu_busy": busy,
-                          "pct_of_peak_at_sclk": 100 * tflops / clock_peak(sclk) if sclk else None}), flush=True)
-        del a, b, c
+    t0 = time.time()
+    while time.time() - t0 < 1.0:  # warm-up: the clock settles under the load
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    calls = max(20, int(seconds * 1e3 / (e0.elapsed_time(e1) / 20)))  # about `seconds` of timed calls
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    sclk, busy = sample_sclk(call, torch, ms) if measure_clock else (None, None)
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"gemm": f"torch.mm bf16 {n}x{n}x{n}", "operands": kind, "calls": calls, "ms_per_call": ms,
+            "tflops": tflops, "pct_of_peak": 100 * tflops / PEAK_BF16_TFLOPS, "sclk_mhz": sclk,
+            "sclk_gpu_busy": busy, "pct_of_peak_at_sclk": 100 * tflops / clock_peak(sclk) if sclk else None}
 
 
 def traffic_entry():
@@ -589,6 +591,8 @@ def main():
                          "the clock depends on operand bit activity (the kernels execute the same instructions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the library GEMM timed after the workloads (gemm_reference in the line)")
     ap.add_argument("--gemm-calibration", action="store_true",
                     help="only time a library bf16 GEMM (torch.mm, 8192^3) on seeded N(0,1) and on constant operands "
                          "for about 2 s each, with the GFX clock: what a dense MFMA load sustains on this box")
@@ -616,7 +620,8 @@ def main():
         log("copied 3 x 1 GiB")
         return
     if args.gemm_calibration:
-        gemm_calibration(torch, not args.no_clock)
+        for kind in ("normal", "constant"):
+            print(json.dumps(gemm_rate(torch, kind, not args.no_clock)), flush=True)
         return
     w = si.WORKLOADS[args.workload]
     main_res = run_workload(w, args.steps, args.warmup, not args.no_clock, args.inputs)
@@ -655,6 +660,10 @@ def main():
                        "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"]) if r["sclk_mhz"] else None),
                        "causal": wx.causal, "layout": wx.layout, "pass": "backward" if wx.backward else "forward"})
 
+    gemm_ref = None
+    if not args.no_gemm_reference:
+        log("timing a library bf16 GEMM on N(0,1) operands for reference")
+        gemm_ref = gemm_rate(torch, "normal", not args.no_clock)
     traffic = traffic_entry()
     roof = {"bound": "mfma", "kernel": "step_mfma_bf16_d128", "achieved": main_res["kernel_tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": main_res["kernel_tflops"] / PEAK_BF16_TFLOPS,
@@ -663,7 +672,9 @@ def main():
                              if main_res["sclk_mhz"] else None),
             "flops_per_launch": sum(main_res["launch_flops"]) / len(main_res["launch_flops"]),
             "launches": len(main_res["launch_ms"]),
-            "avg_launch_ms": sum(main_res["launch_ms"]) / len(main_res["launch_ms"])}
+            "avg_launch_ms": sum(main_res["launch_ms"]) / len(main_res["launch_ms"]),
+            # the same kernel rate against what a softmax-free library GEMM sustains on N(0,1) bf16 here
+            "frac_of_gemm_reference": (main_res["kernel_tflops"] / gemm_ref["tflops"] if gemm_ref else None)}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -685,7 +696,7 @@ def main():
         "sclk_gpu_busy": main_res["sclk_busy"],
         "pct_of_peak_at_sclk": (100 * main_res["tflops"] / clock_peak(main_res["sclk_mhz"])
                                 if main_res["sclk_mhz"] else None),
-        "roofline": roof, "cpu_baseline": cpu, "extra": extras,
+        "roofline": roof, "cpu_baseline": cpu, "gemm_reference": gemm_ref, "extra": extras,
     }
     print(json.dumps(line), flush=True)
 
