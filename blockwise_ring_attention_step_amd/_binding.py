@@ -49,7 +49,9 @@ class RingAttnError(RuntimeError):
 
 
 def lib_path() -> str:
-    return _LIB_FILE
+    """The library this process loads: the in-tree build, or the build of the same sources that
+    RING_ATTN_LIBRARY names (the host-sanitized build of the CPU tests is loaded that way)."""
+    return os.environ.get("RING_ATTN_LIBRARY") or _LIB_FILE
 
 
 def lib() -> ctypes.CDLL:
@@ -57,9 +59,10 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_FILE):
-        raise RuntimeError(f"{_LIB_FILE} is missing: build it with `python -m blockwise_ring_attention_step_amd.build`")
-    L = ctypes.CDLL(_LIB_FILE)
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m blockwise_ring_attention_step_amd.build`")
+    L = ctypes.CDLL(path)
     i32, i64, f32, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     p64 = ctypes.POINTER(ctypes.c_int64)
     L.ring_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, p64, i64,
