@@ -21,7 +21,7 @@ runs count only the visible pairs; the backward counts 10*D (five products of th
 feed-forward 4 d_model d_ff per token (two products).  Printed on stdout: one JSON line.  Progress goes to stderr.
 
 The line also carries ``gemm_reference``: a library bf16 GEMM (torch.mm, 8192^3) timed on seeded N(0,1)
-operands after the workloads, with its clock, and ``roofline.frac_of_gemm_reference``, the step kernel's
+operands before the workloads, with its clock, and ``roofline.frac_of_gemm_reference``, the step kernel's
 rate over that GEMM's (``--no-gemm-reference`` skips it).
 
 Diagnostics (no benchmark line): ``--copy-calibration`` (a plain 1 GiB copy, the reference for HBM byte
@@ -86,7 +86,7 @@ def shard_np(x, P, layout):
     return np.ascontiguousarray(y)
 
 
-def run_workload(w, steps, warmup, measure_clock=True, inputs="normal"):
+def run_workload(w, steps, warmup, measure_clock=True, inputs="normal", before_warmup=None):
     import numpy as np
     import torch
 
@@ -133,6 +133,9 @@ def run_workload(w, steps, warmup, measure_clock=True, inputs="normal"):
         ra.ring_attn_local(tq, tk, tv, o, lse, ws, P=w.P, dev0=dev0, scale=scale, causal=causal, layout=w.layout,
                            compute_stream=cs, copy_stream=xs, step_events=events)
 
+    if before_warmup is not None:  # GPU work of the caller's, run between the upload and the warm-up
+        before_warmup()
+        torch.cuda.synchronize()
     if warmup is None or steps is None:
         # time-bounded extra workload: about 1 s of warm-up and 2 s of timed calls, 3 to 50 calls each
         call()
@@ -592,7 +595,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--no-gemm-reference", action="store_true",
-                    help="skip the library GEMM timed after the workloads (gemm_reference in the line)")
+                    help="skip the library GEMM timed before the workloads (gemm_reference in the line)")
     ap.add_argument("--gemm-calibration", action="store_true",
                     help="only time a library bf16 GEMM (torch.mm, 8192^3) on seeded N(0,1) and on constant operands "
                          "for about 2 s each, with the GFX clock: what a dense MFMA load sustains on this box")
@@ -624,7 +627,22 @@ def main():
             print(json.dumps(gemm_rate(torch, kind, not args.no_clock)), flush=True)
         return
     w = si.WORKLOADS[args.workload]
-    main_res = run_workload(w, args.steps, args.warmup, not args.no_clock, args.inputs)
+    # The reference GEMM runs right before the workload's warm-up (its inputs already on the GPU): besides
+    # its own figure, its seconds of dense load bring the GPU out of idle, so that the warm-up calls
+    # start at the clock the GPU holds under load.
+    gemm_ref = None
+
+    def reference():
+        nonlocal gemm_ref
+        log("timing a library bf16 GEMM on N(0,1) operands for reference")
+        try:
+            gemm_ref = gemm_rate(torch, "normal", not args.no_clock)
+        except Exception as e:  # context only: the benchmark line does not depend on it
+            log(f"library GEMM reference failed ({e!r}); gemm_reference is null")
+            torch.cuda.synchronize()
+
+    main_res = run_workload(w, args.steps, args.warmup, not args.no_clock, args.inputs,
+                            before_warmup=None if args.no_gemm_reference else reference)
     extras = []
     for name in [x for x in args.extra.split(",") if x]:
         if name == "merge_phase_16k":
@@ -660,14 +678,6 @@ def main():
                        "pct_of_peak_at_sclk": (100 * r["tflops"] / clock_peak(r["sclk_mhz"]) if r["sclk_mhz"] else None),
                        "causal": wx.causal, "layout": wx.layout, "pass": "backward" if wx.backward else "forward"})
 
-    gemm_ref = None
-    if not args.no_gemm_reference:
-        log("timing a library bf16 GEMM on N(0,1) operands for reference")
-        try:
-            gemm_ref = gemm_rate(torch, "normal", not args.no_clock)
-        except Exception as e:  # context only: the benchmark line does not depend on it
-            log(f"library GEMM reference failed ({e!r}); gemm_reference is null")
-            torch.cuda.synchronize()
     traffic = traffic_entry()
     roof = {"bound": "mfma", "kernel": "step_mfma_bf16_d128", "achieved": main_res["kernel_tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": main_res["kernel_tflops"] / PEAK_BF16_TFLOPS,
